@@ -1,0 +1,33 @@
+"""Build the CPU oracle's shared library (test infrastructure only).
+
+Plain gcc, -O2, OpenMP, IEEE arithmetic (no fast-math): the oracle must be
+the straightforward definition, not a tuned kernel.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "liboracle.so")
+SRCS = [os.path.join(HERE, "dilated_oracle.c")]
+DEPS = SRCS + [os.path.join(HERE, "oracle_core.inc")]
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile oracle/liboracle.so. Returns its path."""
+    if not force and os.path.exists(LIB):
+        newest = max(os.path.getmtime(p) for p in DEPS)
+        if os.path.getmtime(LIB) >= newest:
+            return LIB
+    tmp = LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+           "-Wno-unused-parameter", "-o", tmp] + SRCS + ["-lm"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True, cwd=HERE)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
