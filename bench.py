@@ -1,0 +1,199 @@
+"""Benchmark of the dilated-attention forward pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one whole forward pass (the attention kernel over every pattern,
+then the log-sum-exp merge) on inputs already resident in GPU memory. W
+untimed steps run first; K steps are then timed between two device
+synchronisations. Inside the timed region HIP events on the launch stream
+bracket the attention kernel of every step, which gives its average launch
+duration for the roofline figure.
+
+Prints one JSON line. `value` is tokens/s (B * N / step time). `roofline`
+reports the attention kernel against the bf16 MFMA peak using the
+algorithmic FLOP count; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dilated-attention fwd tokens/sec and % bf16 MFMA peak at N=32K, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_paper_mixture_n32768.json")
+KERNEL_SOURCES = ["attn_kernel.hip", "da_common.hpp"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_long_sequence_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, heads):
+    """The oracle (as it stands) on the first `heads` heads of the workload:
+    heads are independent, so the full workload costs H / heads times as much."""
+    import numpy as np
+
+    import oracle
+    from sparse_long_sequence_attn_amd.workloads import host_inputs
+
+    q, k, v = host_inputs(w)
+    q, k, v = (np.ascontiguousarray(x[:, :, :heads]) for x in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.fwd(q, k, v, w.patterns, causal=w.causal)
+    dt = time.perf_counter() - t0
+    full = dt * w.H / heads
+    return {
+        "value": w.tokens / full,
+        "unit": "tokens/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"heads 0-{heads - 1} of {w.H} of the same workload (all {w.B * w.N} tokens, "
+                  f"all patterns), fp64 C oracle, {dt:.2f} s measured, scaled by {w.H}/{heads}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="paper_mixture_n32768_h16_bf16")
+    ap.add_argument("--cpu-heads", type=int, default=16,
+                    help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after the timed region, run one device copy of this many MiB "
+                         "(a known-size kernel for scaling rocprofv3 byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the method's sequence-parallel split across GPUs is not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_long_sequence_attn_amd import Problem
+    from sparse_long_sequence_attn_amd.costs import PEAK_HBM_GBS, cost, peak_tflops
+    from sparse_long_sequence_attn_amd.workloads import WORKLOADS, device_inputs, host_inputs, to_torch
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if w.device_generated:
+        q, k, v = device_inputs(w)
+    else:
+        q, k, v = (to_torch(x, dev) for x in host_inputs(w))
+    prob = Problem(q, k, v, w.patterns, w.causal)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        prob.attention_stage(stream)
+        prob.merge_stage(stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        prob.attention_stage(stream)
+        ev[i][1].record(stream)
+        prob.merge_stage(stream)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / K
+    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    merge_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    c = cost(w.B, w.N, w.H, w.Dh, w.patterns, w.causal, 2 if w.dtype == "bf16" else 4)
+    tokens_s = w.tokens / (ms_step / 1e3)
+    peak = peak_tflops(w.dtype)
+    attn_tflops = c.flops_alg / (attn_ms / 1e3) / 1e12
+    step_tflops_alg = c.flops_alg / (ms_step / 1e3) / 1e12
+    step_tflops_ns = c.flops_ns / (ms_step / 1e3) / 1e12
+    mfma_bound = len(w.patterns) > 1 or max(
+        -(-min(pw, w.N) // r) for pw, r in w.patterns) > 256
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(attn_tflops / peak, 4)}
+    else:
+        gbs = c.attn_bytes / (attn_ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "attn_fwd_kernel"
+    roof["kernel_ms"] = round(attn_ms, 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal q, k, v; see workloads.py)",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H": w.H, "Dh": w.Dh,
+                   "patterns": [list(p) for p in w.patterns], "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "roofline": roof,
+        "detail": {
+            "tflops_algorithmic_step": round(step_tflops_alg, 2),
+            "tflops_north_star_formula_step": round(step_tflops_ns, 2),
+            "pct_bf16_peak_algorithmic_step": round(100 * step_tflops_alg / peak, 2),
+            "pct_bf16_peak_north_star_formula_step": round(100 * step_tflops_ns / peak, 2),
+            "flops_algorithmic": c.flops_alg,
+            "flops_north_star_formula": c.flops_ns,
+            "attn_kernel_ms": round(attn_ms, 4),
+            "merge_kernel_ms": round(merge_ms, 4),
+            "attn_algorithmic_bytes": c.attn_bytes,
+            "attn_gbs_algorithmic": round(c.attn_bytes / (attn_ms / 1e3) / 1e9, 1),
+            "merge_algorithmic_bytes": c.merge_bytes,
+            "merge_gbs_algorithmic": round(c.merge_bytes / (merge_ms / 1e3) / 1e9, 1)
+            if merge_ms > 0 and c.merge_bytes > 0 else None,
+            "device": torch.cuda.get_device_name(dev),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

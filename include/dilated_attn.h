@@ -1,0 +1,146 @@
+/*
+ * dilated_attn.h — C ABI of the MI355X (gfx950) dilated-attention forward pass.
+ *
+ * The operation (sources: "LONGNET: Scaling Transformer to 1 billion tokens"
+ * blog, sections "LongNet's attention allocation principle" and the
+ * multi-head paragraph after it; "LongNet论文精读" page, section
+ * "Dilated Attention的工作原理", steps 1-4; dakule.com news page, sections
+ * "如何做到？" and "实验评估"):
+ *
+ *   For every pattern (w, r): w' = min(w, N); the sequence is cut into N/w'
+ *   segments of w' tokens. Head h gathers, inside each segment, the rows at
+ *   offsets (h mod r) + m*r < w' (m = 0 .. L-1, L = ceil((w' - h mod r) / r)),
+ *   runs softmax attention among them (causal over the gathered order when
+ *   asked), and scatters the result back to those rows. The per-pattern
+ *   results O_i with log-sum-exp lse_i of each row are then merged:
+ *       LSE = log(sum_i exp(lse_i)),  out = sum_i exp(lse_i - LSE) * O_i
+ *   over the patterns that gather the row; rows no pattern gathers get
+ *   out = 0 and lse = -inf. The pages do not print the merge weights; this
+ *   weighting by each pattern's softmax denominator is the reading this
+ *   library implements.
+ *
+ * Layout (all row-major, contiguous):
+ *   q, k, v, out : [B, N, H, Dh], one element type for all four
+ *                  (DA_F32: float, DA_BF16: bfloat16), dim = H * Dh.
+ *   lse          : [B, H, N] float, natural logarithm.
+ * Scores are scale * (q . k); scale <= 0 selects 1/sqrt(Dh).
+ *
+ * Memory and ownership: every pointer except `patterns` (host) and the
+ * stream handle is DEVICE memory owned by the caller. The library allocates
+ * nothing, keeps no pointer after a call returns and has no mutable global
+ * state, so calls on different streams may run concurrently as long as they
+ * do not share output or workspace buffers.
+ *
+ * Asynchrony: compute calls enqueue kernels on `stream` (a hipStream_t; NULL
+ * is the default stream) and return without synchronising. Faults during
+ * execution surface at the caller's next synchronisation.
+ *
+ * Errors: every call validates all arguments before launching anything; on
+ * a non-zero return nothing was launched and nothing was written.
+ */
+#ifndef DILATED_ATTN_H
+#define DILATED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DA_VERSION 1
+#define DA_MAX_PATTERNS 8
+#define DA_HEAD_DIM 64
+
+/* One (segment length, dilation rate) pattern. w >= 1, r >= 1 and
+ * r <= min(w, N); N must be a multiple of min(w, N). */
+typedef struct {
+  int32_t w;
+  int32_t r;
+} da_pattern;
+
+enum { DA_F32 = 0, DA_BF16 = 1 };
+
+enum {
+  DA_OK = 0,
+  DA_ERR_NULL = -1,      /* a required pointer is NULL                          */
+  DA_ERR_SHAPE = -2,     /* B, N or H negative, N not a multiple of min(w, N),  */
+                         /* or sizes beyond the supported range                 */
+  DA_ERR_PATTERN = -3,   /* n_patterns outside 1..DA_MAX_PATTERNS, w < 1,       */
+                         /* r < 1 or r > min(w, N)                              */
+  DA_ERR_DTYPE = -4,     /* dtype is not DA_F32 or DA_BF16                      */
+  DA_ERR_HEADDIM = -5,   /* Dh != DA_HEAD_DIM                                   */
+  DA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than required             */
+  DA_ERR_ALIGN = -7,     /* q, k, v, out not 16-byte, lse not 4-byte, or        */
+                         /* workspace not 256-byte aligned                      */
+  DA_ERR_ALIAS = -8,     /* out, lse or workspace overlaps an input or another  */
+                         /* output                                              */
+  DA_ERR_ARG = -9,       /* other invalid scalar (scale not finite, causal not  */
+                         /* 0/1, capacity too small)                            */
+  DA_ERR_LAUNCH = -10    /* the HIP runtime rejected a kernel launch            */
+};
+
+/* Bytes of device workspace dilated_attn_fwd needs for this problem (0 for
+ * a single pattern, whose kernel writes out and lse directly). For two or
+ * more patterns it holds each pattern's per-row partial output (float, Dh
+ * per gathered row) and log-sum-exp before the merge. Writes *bytes and
+ * returns DA_OK, or an error code for invalid arguments. */
+int dilated_attn_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
+                                 const da_pattern* patterns, int32_t n_patterns, int32_t dtype,
+                                 size_t* bytes);
+
+/* The whole forward pass: dilated attention for every pattern, then the
+ * log-sum-exp merge. Writes every element of out and lse. causal is 0 or 1.
+ * workspace: device memory of at least dilated_attn_workspace_bytes() bytes,
+ * 256-byte aligned (may be NULL when that size is 0); its contents on entry
+ * are ignored. Returns DA_OK or a DA_ERR_* code. */
+int dilated_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns,
+                     int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two stages of dilated_attn_fwd, exposed separately so a caller can
+ * time each kernel with events between them. Same arguments and checks as
+ * dilated_attn_fwd; calling _attention then _merge on one stream with the
+ * same arguments is exactly dilated_attn_fwd.
+ *  _attention: one launch covering every pattern. With one pattern it writes
+ *              out and lse; with more it writes the workspace partials.
+ *  _merge:     combines the workspace partials into out and lse; does
+ *              nothing for a single pattern. */
+int dilated_attn_fwd_attention(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int64_t B, int64_t N, int32_t H, int32_t Dh,
+                               const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                               int32_t dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int dilated_attn_fwd_merge(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int64_t B, int64_t N, int32_t H, int32_t Dh,
+                           const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                           int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Test hook: the gather map the kernels use, written by a device kernel
+ * through the same index function as the attention kernel.
+ * dev_out: device int64 [N / min(w, N)][ceil(min(w, N) / r)], segment-major;
+ * entry [s][m] is the sequence position of gathered row m of segment s for
+ * head h, or -1 where m >= L(h). cap is dev_out's length in elements and must
+ * be at least that size. */
+int dilated_attn_gather_map(int64_t N, int32_t H, da_pattern pattern, int32_t h, int64_t* dev_out,
+                            int64_t cap, void* stream);
+
+/* Test hook: the inverse map the merge kernel uses. dev_out: device int64
+ * [N]; entry t is s * ceil(min(w, N) / r) + m when position t is gathered
+ * row m of segment s for head h, else -1. cap must be at least N. */
+int dilated_attn_coverage_map(int64_t N, int32_t H, da_pattern pattern, int32_t h,
+                              int64_t* dev_out, int64_t cap, void* stream);
+
+/* Static description of an error code (never NULL). */
+const char* dilated_attn_strerror(int code);
+
+/* DA_VERSION of the built library. */
+int dilated_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DILATED_ATTN_H */

@@ -1,0 +1,128 @@
+"""Dilated attention (LongNet) forward pass for AMD MI355X (gfx950).
+
+Python face of the C-ABI library: ``dilated_attn`` takes projected q, k, v
+of shape [B, N, H, 64] (bf16 or fp32, on the GPU) and a list of
+(segment length w, dilation r) patterns, and returns (out [B, N, H, 64],
+lse [B, H, N] float32). All computation happens in the HIP kernels; torch
+only allocates memory and supplies the current stream.
+"""
+from . import _native
+from ._native import (DA_BF16, DA_F32, DA_HEAD_DIM, DA_MAX_PATTERNS, DilatedAttnError,
+                      load_library, strerror, version, workspace_bytes)
+
+__all__ = [
+    "dilated_attn", "dilated_attn_attention_stage", "dilated_attn_merge_stage", "gather_map",
+    "coverage_map", "workspace_bytes", "strerror", "version", "load_library", "DilatedAttnError",
+    "DA_F32", "DA_BF16", "DA_HEAD_DIM", "DA_MAX_PATTERNS", "Problem",
+]
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return DA_BF16
+    if t.dtype == torch.float32:
+        return DA_F32
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {t.dtype}")
+
+
+class Problem:
+    """Validated tensors and buffers of one forward call (reusable across
+    calls with the same shapes, e.g. in a timing loop)."""
+
+    def __init__(self, q, k, v, patterns, causal=True, scale=None, out=None, lse=None,
+                 workspace=None):
+        import torch
+
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be on the GPU (got {t.device}); no CPU path exists")
+            if t.dim() != 4 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [B, N, H, Dh] tensor")
+        if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+            raise ValueError("q, k, v must share shape and dtype")
+        if not (q.device == k.device == v.device):
+            raise ValueError("q, k, v must be on one device")
+        self.q, self.k, self.v = q, k, v
+        self.B, self.N, self.H, self.Dh = (int(x) for x in q.shape)
+        self.patterns = [(int(w), int(r)) for (w, r) in patterns]
+        self.causal = bool(causal)
+        self.scale = float(scale) if scale else 0.0
+        self.dtype = _dtype_code(q)
+        self._pats = _native.pattern_array(self.patterns)
+        ws = workspace_bytes(self.B, self.N, self.H, self.Dh, self.patterns, self.dtype)
+        self.out = out if out is not None else torch.empty_like(q)
+        self.lse = lse if lse is not None else torch.empty(
+            (self.B, self.H, self.N), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
+        self.ws_bytes = workspace.numel() * workspace.element_size()
+        if self.out.shape != q.shape or self.out.dtype != q.dtype or not self.out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor like q")
+        if self.lse.shape != (self.B, self.H, self.N) or self.lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, H, N]")
+
+    def _call(self, fn_name, stream=None):
+        import torch
+
+        lib = load_library()
+        if stream is None:
+            stream = torch.cuda.current_stream(self.q.device)
+        code = getattr(lib, fn_name)(
+            self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
+            self.lse.data_ptr(), self.B, self.N, self.H, self.Dh, self._pats, len(self.patterns),
+            1 if self.causal else 0, self.dtype, self.scale, self.workspace.data_ptr(),
+            self.ws_bytes, stream.cuda_stream)
+        _native.check(code, fn_name)
+
+    def run(self, stream=None):
+        self._call("dilated_attn_fwd", stream)
+        return self.out, self.lse
+
+    def attention_stage(self, stream=None):
+        self._call("dilated_attn_fwd_attention", stream)
+
+    def merge_stage(self, stream=None):
+        self._call("dilated_attn_fwd_merge", stream)
+
+
+def dilated_attn(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, workspace=None):
+    """Dilated-attention forward. Returns (out, lse); see include/dilated_attn.h."""
+    return Problem(q, k, v, patterns, causal, scale, out, lse, workspace).run()
+
+
+def dilated_attn_attention_stage(prob, stream=None):
+    prob.attention_stage(stream)
+
+
+def dilated_attn_merge_stage(prob, stream=None):
+    prob.merge_stage(stream)
+
+
+def _map(fn_name, N, H, pattern, h, size, device):
+    import torch
+
+    out = torch.empty(max(size, 1), dtype=torch.int64, device=device)
+    lib = load_library()
+    code = getattr(lib, fn_name)(int(N), int(H), _native.DaPattern(int(pattern[0]), int(pattern[1])),
+                                 int(h), out.data_ptr(), out.numel(),
+                                 torch.cuda.current_stream(out.device).cuda_stream)
+    _native.check(code, fn_name)
+    return out[:size]
+
+
+def gather_map(N, H, pattern, h, device="cuda"):
+    """Device dump of the gather map: int64 [nseg, lmax], -1 past L(h)."""
+    w, r = pattern
+    wp = min(int(w), int(N))
+    nseg, lmax = int(N) // wp, -(-wp // int(r))
+    return _map("dilated_attn_gather_map", N, H, pattern, h, nseg * lmax, device).view(nseg, lmax)
+
+
+def coverage_map(N, H, pattern, h, device="cuda"):
+    """Device dump of the inverse map: int64 [N], compact index or -1."""
+    return _map("dilated_attn_coverage_map", N, H, pattern, h, int(N), device)

@@ -1,0 +1,316 @@
+// C ABI of the dilated-attention library: argument validation, the launch
+// plan (pattern geometry, tile order, workspace layout) and the launches.
+// Every check runs before the first launch, so a failing call launches and
+// writes nothing. The library keeps no state between calls.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "da_common.hpp"
+#include "dilated_attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+using da::kDh;
+using da::kMaxPat;
+using da::PatDev;
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct Plan {
+  bool empty = false;
+  bool bf16 = false;
+  bool causal = true;
+  int nw = 4;
+  int np = 0;
+  int64_t B = 0, N = 0;
+  int32_t H = 0;
+  float sl2 = 0.f;
+  PatDev pat[kMaxPat];     // caller's order
+  int order[kMaxPat];      // pattern indices sorted by ntile, descending
+  int64_t unit_prefix[kMaxPat + 1];
+  int64_t band_start[kMaxPat + 1];
+  int64_t total_tiles = 0;
+  size_t ws_bytes = 0;
+  size_t tensor_bytes = 0;
+  size_t lse_bytes = 0;
+};
+
+int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
+
+// Shapes, patterns, dtype and scalars; computes everything that does not
+// depend on pointers.
+int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns,
+              int32_t n_patterns, int32_t causal, int32_t dtype, float scale, Plan* pl) {
+  if (dtype != DA_F32 && dtype != DA_BF16) return DA_ERR_DTYPE;
+  if (Dh != DA_HEAD_DIM) return DA_ERR_HEADDIM;
+  if (n_patterns < 1 || n_patterns > DA_MAX_PATTERNS) return DA_ERR_PATTERN;
+  if (!patterns) return DA_ERR_NULL;
+  if (B < 0 || N < 0 || H < 0) return DA_ERR_SHAPE;
+  // sizes the kernels index with 32-bit positions and grid dimensions
+  if (N > kMaxGrid || H > 65535 || B > 65535 || N * (int64_t)H > kMaxGrid) return DA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return DA_ERR_ARG;
+  if (!isfinite(scale)) return DA_ERR_ARG;
+  for (int i = 0; i < n_patterns; ++i) {
+    if (patterns[i].w < 1 || patterns[i].r < 1) return DA_ERR_PATTERN;
+    if (N > 0) {
+      const int64_t wp = std::min<int64_t>(patterns[i].w, N);
+      if (N % wp != 0) return DA_ERR_SHAPE;
+      if (patterns[i].r > wp) return DA_ERR_PATTERN;
+    }
+  }
+  pl->bf16 = dtype == DA_BF16;
+  pl->causal = causal != 0;
+  pl->np = n_patterns;
+  pl->B = B;
+  pl->N = N;
+  pl->H = H;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)Dh);
+  pl->sl2 = (float)(sc * (double)kLog2e);
+  pl->tensor_bytes = (size_t)(B * N * H * Dh) * (pl->bf16 ? 2 : 4);
+  pl->lse_bytes = (size_t)(B * N * H) * 4;
+  pl->empty = B == 0 || N == 0 || H == 0;
+  if (pl->empty) return DA_OK;
+
+  int32_t lmax_all = 0;
+  for (int i = 0; i < n_patterns; ++i) {
+    PatDev& p = pl->pat[i];
+    memset(&p, 0, sizeof p);
+    p.wp = std::min<int64_t>(patterns[i].w, N);
+    p.nseg = N / p.wp;
+    p.r = patterns[i].r;
+    p.lmax = da::rows_gathered(p.wp, 0, p.r);
+    p.units = B * H * p.nseg;
+    p.wp_div = da::make_fastdiv((uint32_t)p.wp);
+    p.r_div = da::make_fastdiv((uint32_t)p.r);
+    lmax_all = std::max(lmax_all, p.lmax);
+  }
+  // one 32-row wave per workgroup when every segment is that short
+  pl->nw = lmax_all > 32 ? 4 : 1;
+  const int bm = da::attn_tile_rows(pl->nw);
+  for (int i = 0; i < n_patterns; ++i) pl->pat[i].ntile = (pl->pat[i].lmax + bm - 1) / bm;
+
+  for (int i = 0; i < n_patterns; ++i) pl->order[i] = i;
+  std::stable_sort(pl->order, pl->order + n_patterns,
+                   [&](int x, int y) { return pl->pat[x].ntile > pl->pat[y].ntile; });
+  pl->unit_prefix[0] = 0;
+  for (int j = 0; j < n_patterns; ++j)
+    pl->unit_prefix[j + 1] = pl->unit_prefix[j] + pl->pat[pl->order[j]].units;
+  pl->band_start[0] = 0;
+  for (int j = 0; j < n_patterns; ++j) {
+    const int64_t hi = pl->pat[pl->order[j]].ntile;
+    const int64_t lo = j + 1 < n_patterns ? pl->pat[pl->order[j + 1]].ntile : 0;
+    pl->band_start[j + 1] = pl->band_start[j] + (hi - lo) * pl->unit_prefix[j + 1];
+  }
+  pl->total_tiles = pl->band_start[n_patterns];
+  if (pl->total_tiles > kMaxGrid) return DA_ERR_SHAPE;
+
+  // partial outputs and log2-sum-exp per pattern, 256-byte aligned regions
+  int64_t cur = 0;
+  if (n_patterns > 1) {
+    for (int i = 0; i < n_patterns; ++i) {
+      PatDev& p = pl->pat[i];
+      const int64_t rows = B * H * p.nseg * p.lmax;
+      p.po_off = cur;
+      cur += align64(rows * kDh);
+      p.pl_off = cur;
+      cur += align64(rows);
+    }
+  }
+  pl->ws_bytes = (size_t)cur * 4;
+  return DA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+int check_buffers(const Plan& pl, const void* q, const void* k, const void* v, const void* out,
+                  const float* lse, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !out || !lse) return DA_ERR_NULL;
+  if (pl.ws_bytes > 0 && !ws) return DA_ERR_WORKSPACE;
+  if (ws_bytes < pl.ws_bytes) return DA_ERR_WORKSPACE;
+  auto mis = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
+  if (mis(q, 16) || mis(k, 16) || mis(v, 16) || mis(out, 16) || mis(lse, 4)) return DA_ERR_ALIGN;
+  if (pl.ws_bytes > 0 && mis(ws, 256)) return DA_ERR_ALIGN;
+  const size_t tb = pl.tensor_bytes, lb = pl.lse_bytes, wb = pl.ws_bytes;
+  const void* ins[3] = {q, k, v};
+  for (const void* in : ins)
+    if (overlaps(out, tb, in, tb) || overlaps(lse, lb, in, tb) || overlaps(ws, wb, in, tb))
+      return DA_ERR_ALIAS;
+  if (overlaps(out, tb, lse, lb) || overlaps(out, tb, ws, wb) || overlaps(lse, lb, ws, wb))
+    return DA_ERR_ALIAS;
+  return DA_OK;
+}
+
+int run_attention(const Plan& pl, const void* q, const void* k, const void* v, void* out,
+                  float* lse, void* ws, hipStream_t st) {
+  da::AttnArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.ws = reinterpret_cast<float*>(ws);
+  a.B = pl.B;
+  a.N = pl.N;
+  a.H = pl.H;
+  a.np = pl.np;
+  a.sl2 = pl.sl2;
+  for (int j = 0; j < pl.np; ++j) a.pat[j] = pl.pat[pl.order[j]];
+  for (int j = 0; j <= pl.np; ++j) {
+    a.unit_prefix[j] = pl.unit_prefix[j];
+    a.band_start[j] = pl.band_start[j];
+  }
+  const hipError_t e =
+      da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.total_tiles, st);
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+int run_merge(const Plan& pl, void* out, float* lse, const void* ws, hipStream_t st) {
+  if (pl.np == 1) return DA_OK;
+  da::MergeArgs m;
+  memset(&m, 0, sizeof m);
+  m.out = out;
+  m.lse = lse;
+  m.ws = reinterpret_cast<const float*>(ws);
+  m.B = pl.B;
+  m.N = pl.N;
+  m.H = pl.H;
+  m.np = pl.np;
+  for (int i = 0; i < pl.np; ++i) m.pat[i] = pl.pat[i];
+  const hipError_t e = da::launch_merge(m, pl.bf16, st);
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+enum Stage { kBoth = 3, kAttention = 1, kMerge = 2 };
+
+int fwd_common(int stages, const void* q, const void* k, const void* v, void* out, float* lse,
+               int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns,
+               int32_t n_patterns, int32_t causal, int32_t dtype, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  Plan pl;
+  int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
+  if (rc != DA_OK || pl.empty) return rc;
+  rc = check_buffers(pl, q, k, v, out, lse, workspace, workspace_bytes);
+  if (rc != DA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (stages & kAttention) {
+    rc = run_attention(pl, q, k, v, out, lse, workspace, st);
+    if (rc != DA_OK) return rc;
+  }
+  if (stages & kMerge) rc = run_merge(pl, out, lse, workspace, st);
+  return rc;
+}
+
+// Geometry of one pattern for the map hooks.
+int map_pattern(int64_t N, int32_t H, da_pattern p, int32_t h, PatDev* out) {
+  if (N < 1 || N > kMaxGrid || H < 1) return DA_ERR_SHAPE;
+  if (h < 0 || h >= H) return DA_ERR_ARG;
+  if (p.w < 1 || p.r < 1) return DA_ERR_PATTERN;
+  const int64_t wp = std::min<int64_t>(p.w, N);
+  if (N % wp != 0) return DA_ERR_SHAPE;
+  if (p.r > wp) return DA_ERR_PATTERN;
+  memset(out, 0, sizeof *out);
+  out->wp = wp;
+  out->nseg = N / wp;
+  out->r = p.r;
+  out->lmax = da::rows_gathered(wp, 0, p.r);
+  out->wp_div = da::make_fastdiv((uint32_t)wp);
+  out->r_div = da::make_fastdiv((uint32_t)p.r);
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dilated_attn_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
+                                 const da_pattern* patterns, int32_t n_patterns, int32_t dtype,
+                                 size_t* bytes) {
+  if (!bytes) return DA_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(B, N, H, Dh, patterns, n_patterns, 1, dtype, 0.f, &pl);
+  if (rc != DA_OK) return rc;
+  *bytes = pl.empty ? 0 : pl.ws_bytes;
+  return DA_OK;
+}
+
+int dilated_attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                     int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns,
+                     int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_common(kBoth, q, k, v, out, lse, B, N, H, Dh, patterns, n_patterns, causal, dtype,
+                    scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_fwd_attention(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int64_t B, int64_t N, int32_t H, int32_t Dh,
+                               const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                               int32_t dtype, float scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return fwd_common(kAttention, q, k, v, out, lse, B, N, H, Dh, patterns, n_patterns, causal,
+                    dtype, scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_fwd_merge(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int64_t B, int64_t N, int32_t H, int32_t Dh,
+                           const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                           int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return fwd_common(kMerge, q, k, v, out, lse, B, N, H, Dh, patterns, n_patterns, causal, dtype,
+                    scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_gather_map(int64_t N, int32_t H, da_pattern pattern, int32_t h, int64_t* dev_out,
+                            int64_t cap, void* stream) {
+  PatDev p;
+  int rc = map_pattern(N, H, pattern, h, &p);
+  if (rc != DA_OK) return rc;
+  if (!dev_out) return DA_ERR_NULL;
+  if (cap < p.nseg * p.lmax) return DA_ERR_ARG;
+  if (((uintptr_t)dev_out & 7) != 0) return DA_ERR_ALIGN;
+  const hipError_t e =
+      da::launch_gather_map(p, h, dev_out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+int dilated_attn_coverage_map(int64_t N, int32_t H, da_pattern pattern, int32_t h,
+                              int64_t* dev_out, int64_t cap, void* stream) {
+  PatDev p;
+  int rc = map_pattern(N, H, pattern, h, &p);
+  if (rc != DA_OK) return rc;
+  if (!dev_out) return DA_ERR_NULL;
+  if (cap < N) return DA_ERR_ARG;
+  if (((uintptr_t)dev_out & 7) != 0) return DA_ERR_ALIGN;
+  const hipError_t e =
+      da::launch_coverage_map(p, h, N, dev_out, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+const char* dilated_attn_strerror(int code) {
+  switch (code) {
+    case DA_OK: return "success";
+    case DA_ERR_NULL: return "a required pointer is NULL";
+    case DA_ERR_SHAPE: return "invalid or unsupported shape (B, N, H, or N not a multiple of min(w, N))";
+    case DA_ERR_PATTERN: return "invalid pattern list (count, w < 1, r < 1 or r > min(w, N))";
+    case DA_ERR_DTYPE: return "unsupported dtype (DA_F32 or DA_BF16)";
+    case DA_ERR_HEADDIM: return "unsupported head dimension (must be 64)";
+    case DA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DA_ERR_ALIGN: return "misaligned pointer";
+    case DA_ERR_ALIAS: return "an output or the workspace overlaps another buffer";
+    case DA_ERR_ARG: return "invalid argument";
+    case DA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown error code";
+  }
+}
+
+int dilated_attn_version(void) { return DA_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Shared host/device definitions of the dilated-attention library:
+// per-launch parameter blocks and the one index function that every kernel
+// (attention, merge, map dumps) uses to place gathered rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace da {
+
+constexpr int kDh = 64;       // head dimension the kernels are built for
+constexpr int kMaxPat = 8;    // patterns per call
+
+// Unsigned 32-bit division by a run-time constant d >= 1 as a multiply-high,
+// add and shift (round-up method of Granlund and Montgomery, "Division by
+// Invariant Integers using Multiplication", PLDI 1994): with s = ceil(log2 d)
+// and m = floor(2^32 (2^s - d) / d) + 1, n / d = (mulhi(n, m) + n) >> s for
+// every n < 2^32 when the addition is carried out in 64 bits.
+struct FastDiv {
+  uint32_t d;
+  uint32_t m;
+  uint32_t s;
+  uint32_t pad_;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while (s < 32 && (uint64_t(1) << s) < d) ++s;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+  return FastDiv{d, (uint32_t)m, s, 0};
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  const uint64_t hi = ((uint64_t)n * f.m) >> 32;
+  return (uint32_t)((hi + n) >> f.s);
+}
+
+// One pattern after planning. Geometry follows the segment / dilation /
+// per-head-offset construction of the LongNet blog ("LongNet's attention
+// allocation principle" and the multi-head paragraph after it).
+struct PatDev {
+  int64_t wp;      // effective segment length min(w, N)
+  int64_t nseg;    // N / wp
+  int64_t units;   // B * H * nseg independent (batch, head, segment) problems
+  int64_t po_off;  // float offset of this pattern's partial outputs in the workspace
+  int64_t pl_off;  // float offset of this pattern's partial log2-sum-exp values
+  int32_t r;       // dilation rate
+  int32_t lmax;    // ceil(wp / r): rows gathered by a head with offset 0
+  int32_t ntile;   // query tiles per segment: ceil(lmax / BM)
+  int32_t pad_;
+  FastDiv wp_div;  // division by wp
+  FastDiv r_div;   // division by r
+};
+
+// Attention launch. Tiles of all patterns share one grid; patterns are
+// stored sorted by ntile (descending) so that block ids can be handed out
+// heaviest tile first (see decode_tile).
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;       // final output (single pattern) - unused otherwise
+  float* lse;      // final lse (single pattern) - unused otherwise
+  float* ws;       // workspace partials (two or more patterns)
+  int64_t B;
+  int64_t N;
+  int32_t H;
+  int32_t np;
+  float sl2;       // softmax scale * log2(e)
+  int32_t pad_;
+  PatDev pat[kMaxPat];
+  int64_t unit_prefix[kMaxPat + 1];  // prefix sums of units in sorted order
+  int64_t band_start[kMaxPat + 1];   // first block id of each band (see decode_tile)
+};
+
+struct MergeArgs {
+  void* out;
+  float* lse;
+  const float* ws;
+  int64_t B;
+  int64_t N;
+  int32_t H;
+  int32_t np;
+  PatDev pat[kMaxPat];  // caller's order (any order gives the same merge)
+};
+
+// ---------------------------------------------------------------- index maps
+
+// Offset of head h inside every segment of a pattern with dilation r.
+__host__ __device__ inline int32_t head_offset(int32_t h, int32_t r) { return h % r; }
+
+// Rows a head with offset off gathers from one segment of length wp.
+__host__ __device__ inline int32_t rows_gathered(int64_t wp, int32_t off, int32_t r) {
+  return off < wp ? (int32_t)((wp - off + r - 1) / r) : 0;
+}
+
+// Sequence position of gathered row m of segment s.
+__host__ __device__ inline int64_t gathered_pos(int64_t s, int64_t wp, int32_t off, int32_t r,
+                                                int64_t m) {
+  return s * wp + off + m * (int64_t)r;
+}
+
+// Inverse of gathered_pos for one head: s * lmax + m if position t is a
+// gathered row, else -1. Positions are below 2^31.
+__host__ __device__ inline int64_t compact_index(uint32_t t, const PatDev& p, int32_t off) {
+  const uint32_t s = fdiv(t, p.wp_div);
+  const int32_t rel = (int32_t)(t - s * p.wp_div.d) - off;
+  if (rel < 0) return -1;
+  const uint32_t m = fdiv((uint32_t)rel, p.r_div);
+  if ((uint32_t)rel != m * (uint32_t)p.r) return -1;
+  return (int64_t)s * p.lmax + m;
+}
+
+}  // namespace da

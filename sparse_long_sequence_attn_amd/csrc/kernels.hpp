@@ -1,0 +1,27 @@
+// Host-side launchers of the library's kernels (defined in attn_kernel.hip
+// and merge_kernel.hip). All launches are asynchronous on the given stream.
+#pragma once
+
+#include "da_common.hpp"
+
+namespace da {
+
+// Query rows per attention workgroup for nw waves.
+int attn_tile_rows(int nw);
+
+// The fused gather / QK^T / online softmax / PV kernel over every tile of
+// every pattern in `a` (grid = total tiles). nw is 4 (128-row tiles, 64-key
+// LDS tiles) or 1 (32-row tiles, 32-key LDS tiles, for short segments).
+hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, bool final_out,
+                            int64_t grid, hipStream_t st);
+
+// Log-sum-exp merge of the per-pattern partials into out and lse.
+hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st);
+
+// Test hooks: dump the gather map / the inverse (coverage) map of one
+// pattern for one head, computed with the kernels' own index functions.
+hipError_t launch_gather_map(const PatDev& p, int32_t h, int64_t* out, hipStream_t st);
+hipError_t launch_coverage_map(const PatDev& p, int32_t h, int64_t N, int64_t* out,
+                               hipStream_t st);
+
+}  // namespace da

@@ -1,0 +1,144 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the
+header declares, and rejects every invalid call before touching HIP.
+
+Pointers here are fake device addresses: validation never dereferences them,
+and every case below fails validation, so no HIP call is made.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sparse_long_sequence_attn_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dilated_attn.h")
+
+A = 1 << 20          # distinct, 256-byte aligned fake device addresses
+Q, K, V, OUT, LSE, WS = (A * i for i in range(1, 7))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(dilated_attn_\w+)\s*\(", text)))
+
+
+def header_constants():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"\b(DA_\w+)\s*=\s*(-?\d+)", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _native.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = header_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_native.SIGNATURES)
+
+
+def test_binding_constants_match_header():
+    c = header_constants()
+    assert c["DA_F32"] == _native.DA_F32 and c["DA_BF16"] == _native.DA_BF16
+    for code, name in _native.ERROR_NAMES.items():
+        assert c[name] == code
+    text = open(HEADER).read()
+    assert int(re.search(r"#define DA_MAX_PATTERNS (\d+)", text)[1]) == _native.DA_MAX_PATTERNS
+    assert int(re.search(r"#define DA_HEAD_DIM (\d+)", text)[1]) == _native.DA_HEAD_DIM
+    assert int(re.search(r"#define DA_VERSION (\d+)", text)[1]) == _native.version()
+
+
+def test_strerror_covers_every_code(lib):
+    seen = set()
+    for code in _native.ERROR_NAMES:
+        s = _native.strerror(code)
+        assert s and s != "unknown error code"
+        seen.add(s)
+    assert len(seen) == len(_native.ERROR_NAMES)
+    assert _native.strerror(12345) == "unknown error code"
+
+
+def fwd(lib, fn="dilated_attn_fwd", q=Q, k=K, v=V, out=OUT, lse=LSE, B=1, N=64, H=4, Dh=64,
+        pats=((16, 2), (32, 4)), npat=None, causal=1, dtype=_native.DA_BF16, scale=0.0, ws=WS,
+        wsb=1 << 30):
+    arr = _native.pattern_array(pats) if pats is not None else None
+    return getattr(lib, fn)(q, k, v, out, lse, B, N, H, Dh, arr,
+                            len(pats) if npat is None else npat, causal, dtype, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["dilated_attn_fwd", "dilated_attn_fwd_attention",
+                                "dilated_attn_fwd_merge"])
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(out=None), -1),
+    (dict(lse=None), -1), (dict(pats=None, npat=1), -1),
+    (dict(B=-1), -2), (dict(N=-4), -2), (dict(H=-1), -2), (dict(N=60), -2),
+    (dict(B=70000), -2), (dict(N=1 << 31), -2),
+    (dict(pats=()), -3), (dict(pats=((16, 2),) * 9), -3), (dict(pats=((0, 1),)), -3),
+    (dict(pats=((16, 0),)), -3), (dict(pats=((8, 9),)), -3), (dict(pats=((128, 65),)), -3),
+    (dict(dtype=2), -4), (dict(dtype=-1), -4),
+    (dict(Dh=128), -5), (dict(Dh=32), -5),
+    (dict(ws=None), -6), (dict(wsb=100), -6),
+    (dict(q=Q + 8), -7), (dict(out=OUT + 4), -7), (dict(lse=LSE + 2), -7), (dict(ws=WS + 64), -7),
+    (dict(out=Q), -8), (dict(lse=K + 64), -8), (dict(ws=V), -8), (dict(out=LSE), -8),
+    (dict(causal=2), -9), (dict(scale=math.inf), -9), (dict(scale=math.nan), -9),
+])
+def test_invalid_calls_rejected(lib, fn, kwargs, code):
+    assert fwd(lib, fn, **kwargs) == code
+
+
+def test_empty_problems_are_accepted_without_launch(lib):
+    # nothing to do: no pointer is needed and nothing is launched
+    for B, N, H in [(0, 64, 4), (1, 0, 4), (1, 64, 0)]:
+        assert fwd(lib, B=B, N=N, H=H, q=None, k=None, v=None, out=None, lse=None, ws=None,
+                   wsb=0) == 0
+
+
+def ws_expected(B, N, H, pats):
+    """Workspace size from the layout the header describes: per pattern, a
+    float partial row (64 values) and a float lse per gathered row slot
+    (segments x ceil(w'/r)), each region rounded up to 256 bytes."""
+    if len(pats) == 1:
+        return 0
+    tot = 0
+    for (w, r) in pats:
+        wp = min(w, N)
+        rows = B * H * (N // wp) * (-(-wp // r))
+        tot += -(-rows * 64 * 4 // 256) * 256 + -(-rows * 4 // 256) * 256
+    return tot
+
+
+@pytest.mark.parametrize("B,N,H,pats", [
+    (1, 512, 8, [(64, 2)]),
+    (4, 8192, 12, [(2048, 1), (4096, 2), (8192, 4)]),
+    (1, 32768, 16, [(2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12)]),
+    (2, 96, 3, [(1000, 7), (8, 1), (96, 96)]),
+])
+def test_workspace_bytes(B, N, H, pats):
+    assert _native.workspace_bytes(B, N, H, 64, pats, _native.DA_BF16) == ws_expected(B, N, H, pats)
+
+
+def test_workspace_bytes_errors(lib):
+    out = ctypes.c_size_t(0)
+    arr = _native.pattern_array([(16, 2)])
+    assert lib.dilated_attn_workspace_bytes(1, 64, 4, 64, arr, 1, 1, None) == -1
+    assert lib.dilated_attn_workspace_bytes(1, 60, 4, 64, arr, 1, 1, ctypes.byref(out)) == -2
+    assert lib.dilated_attn_workspace_bytes(1, 64, 4, 32, arr, 1, 1, ctypes.byref(out)) == -5
+
+
+@pytest.mark.parametrize("fn", ["dilated_attn_gather_map", "dilated_attn_coverage_map"])
+def test_map_hooks_validate(lib, fn):
+    f = getattr(lib, fn)
+    p = _native.DaPattern(16, 2)
+    assert f(64, 4, p, 0, None, 1 << 20, None) == -1
+    assert f(60, 4, p, 0, A, 1 << 20, None) == -2
+    assert f(64, 4, _native.DaPattern(16, 0), 0, A, 1 << 20, None) == -3
+    assert f(64, 4, p, 4, A, 1 << 20, None) == -9
+    assert f(64, 4, p, -1, A, 1 << 20, None) == -9
+    assert f(64, 4, p, 0, A, 3, None) == -9
+    assert f(64, 4, p, 0, A + 4, 1 << 20, None) == -7
