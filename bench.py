@@ -128,8 +128,10 @@ def main():
     t1 = time.perf_counter()
 
     ms_step = (t1 - t0) * 1e3 / K
-    attn_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    merge_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    attn_times = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    merge_times = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    attn_ms = sum(attn_times) / K
+    merge_ms = sum(merge_times) / K
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -181,7 +183,9 @@ def main():
             "flops_algorithmic": c.flops_alg,
             "flops_north_star_formula": c.flops_ns,
             "attn_kernel_ms": round(attn_ms, 4),
+            "attn_kernel_ms_median": round(attn_times[K // 2], 4),
             "merge_kernel_ms": round(merge_ms, 4),
+            "merge_kernel_ms_median": round(merge_times[K // 2], 4),
             "attn_algorithmic_bytes": c.attn_bytes,
             "attn_gbs_algorithmic": round(c.attn_bytes / (attn_ms / 1e3) / 1e9, 1),
             "merge_algorithmic_bytes": c.merge_bytes,
