@@ -22,6 +22,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no accvgpr copies around the
+    # softmax and fewer registers (three waves per SIMD instead of two)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

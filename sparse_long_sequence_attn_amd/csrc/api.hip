@@ -31,9 +31,9 @@ struct Plan {
   float sl2 = 0.f;
   PatDev pat[kMaxPat];     // caller's order
   int order[kMaxPat];      // pattern indices sorted by ntile, descending
-  int64_t unit_prefix[kMaxPat + 1];
-  int64_t band_start[kMaxPat + 1];
+  int64_t unit_start[kMaxPat + 1];
   int64_t total_tiles = 0;
+  int64_t grid = 0;  // kXcds * (longest per-XCD tile list)
   size_t ws_bytes = 0;
   size_t tensor_bytes = 0;
   size_t lse_bytes = 0;
@@ -96,17 +96,28 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
   for (int i = 0; i < n_patterns; ++i) pl->order[i] = i;
   std::stable_sort(pl->order, pl->order + n_patterns,
                    [&](int x, int y) { return pl->pat[x].ntile > pl->pat[y].ntile; });
-  pl->unit_prefix[0] = 0;
+  pl->unit_start[0] = 0;
   for (int j = 0; j < n_patterns; ++j)
-    pl->unit_prefix[j + 1] = pl->unit_prefix[j] + pl->pat[pl->order[j]].units;
-  pl->band_start[0] = 0;
+    pl->unit_start[j + 1] = pl->unit_start[j] + pl->pat[pl->order[j]].units;
+  // per-XCD tile lists (units dealt round-robin in sorted order)
+  int64_t per_xcd[da::kXcds] = {0};
   for (int j = 0; j < n_patterns; ++j) {
-    const int64_t hi = pl->pat[pl->order[j]].ntile;
-    const int64_t lo = j + 1 < n_patterns ? pl->pat[pl->order[j + 1]].ntile : 0;
-    pl->band_start[j + 1] = pl->band_start[j] + (hi - lo) * pl->unit_prefix[j + 1];
+    const PatDev& p = pl->pat[pl->order[j]];
+    for (int x = 0; x < da::kXcds; ++x) {
+      const int64_t u0 = pl->unit_start[j], u1 = pl->unit_start[j + 1];
+      const int64_t first = u0 + (((x - u0) % da::kXcds) + da::kXcds) % da::kXcds;
+      const int64_t cnt = first < u1 ? (u1 - first + da::kXcds - 1) / da::kXcds : 0;
+      per_xcd[x] += cnt * p.ntile;
+    }
   }
-  pl->total_tiles = pl->band_start[n_patterns];
-  if (pl->total_tiles > kMaxGrid) return DA_ERR_SHAPE;
+  pl->total_tiles = 0;
+  int64_t longest = 0;
+  for (int x = 0; x < da::kXcds; ++x) {
+    pl->total_tiles += per_xcd[x];
+    longest = std::max(longest, per_xcd[x]);
+  }
+  pl->grid = longest * da::kXcds;
+  if (pl->grid > kMaxGrid) return DA_ERR_SHAPE;
 
   // partial outputs and log2-sum-exp per pattern, 256-byte aligned regions
   int64_t cur = 0;
@@ -164,12 +175,9 @@ int run_attention(const Plan& pl, const void* q, const void* k, const void* v, v
   a.np = pl.np;
   a.sl2 = pl.sl2;
   for (int j = 0; j < pl.np; ++j) a.pat[j] = pl.pat[pl.order[j]];
-  for (int j = 0; j <= pl.np; ++j) {
-    a.unit_prefix[j] = pl.unit_prefix[j];
-    a.band_start[j] = pl.band_start[j];
-  }
+  for (int j = 0; j <= pl.np; ++j) a.unit_start[j] = pl.unit_start[j];
   const hipError_t e =
-      da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.total_tiles, st);
+      da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.grid, st);
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 

@@ -44,30 +44,32 @@ struct Tile {
   int32_t qt;   // query tile inside the segment
 };
 
-// Block id -> tile, heaviest causal tiles first. Patterns are sorted by
-// ntile (n_0 >= n_1 >= ...). Tile level qt costs (qt + 1) key tiles for
-// every pattern, so the ids walk levels from the top: band j holds levels
-// n_j - 1 down to n_{j+1}, in which patterns 0..j are active, each level
-// holding unit_prefix[j + 1] tiles.
-__device__ inline Tile decode_tile(const AttnArgs& a, int64_t id) {
-  int j = 0;
-  while (j + 1 < a.np && id >= a.band_start[j + 1]) ++j;
-  const int64_t rel = id - a.band_start[j];
-  const int64_t per = a.unit_prefix[j + 1];
-  const int64_t lvl = rel / per;
-  int64_t rem = rel - lvl * per;
-  int p = 0;
-  while (rem >= a.unit_prefix[p + 1]) ++p;
-  rem -= a.unit_prefix[p];
-  const int64_t nseg = a.pat[p].nseg;
-  Tile t;
-  t.seg = rem % nseg;
-  const int64_t bh = rem / nseg;
-  t.h = (int32_t)(bh % a.H);
-  t.b = bh / a.H;
-  t.p = p;
-  t.qt = (int32_t)(a.pat[j].ntile - 1 - lvl);
-  return t;
+// Block id -> tile (see AttnArgs for the order). Returns false for the
+// padding blocks of XCDs whose list is shorter than the longest one.
+__device__ inline bool decode_tile(const AttnArgs& a, int64_t id, Tile* t) {
+  const int32_t x = (int32_t)(id % kXcds);
+  int64_t slot = id / kXcds;
+  for (int p = 0; p < a.np; ++p) {
+    const int64_t u0 = a.unit_start[p], u1 = a.unit_start[p + 1];
+    // first unit of this pattern dealt to XCD x, and how many it gets
+    const int64_t first = u0 + (((x - u0) % kXcds) + kXcds) % kXcds;
+    const int64_t cnt = first < u1 ? (u1 - first + kXcds - 1) / kXcds : 0;
+    const int64_t nt = a.pat[p].ntile;
+    if (slot < cnt * nt) {
+      const int64_t lu = slot / nt;
+      const int64_t rem = first + lu * kXcds - u0;  // unit index inside the pattern
+      const int64_t nseg = a.pat[p].nseg;
+      t->seg = rem % nseg;
+      const int64_t bh = rem / nseg;
+      t->h = (int32_t)(bh % a.H);
+      t->b = bh / a.H;
+      t->p = p;
+      t->qt = (int32_t)(nt - 1 - (slot - lu * nt));
+      return true;
+    }
+    slot -= cnt * nt;
+  }
+  return false;
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -105,7 +107,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   T* const Ks = reinterpret_cast<T*>(smem);
   T* const Vs = Ks + 2 * SM::kKElems;
 
-  const Tile tl = decode_tile(a, blockIdx.x);
+  Tile tl;
+  if (!decode_tile(a, blockIdx.x, &tl)) return;
   const PatDev& P = a.pat[tl.p];
   const int32_t r = P.r;
   const int64_t wp = P.wp;
@@ -134,6 +137,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   const int32_t nkt_w = qw0 >= L ? 0 : (CAUSAL ? (qend_w + BN - 1) / BN : nkt);
   const int32_t mq = qw0 + n;  // this lane's query (gathered index)
   const bool qvalid = mq < L;
+  // Rows past L are read from row L-1 instead of being skipped: keys past L
+  // are masked and queries past L are never stored, so no load needs a branch.
+  const int32_t mqc = min(mq, L - 1);
 
   const T* const Qg = reinterpret_cast<const T*>(a.q);
   const T* const Kg = reinterpret_cast<const T*>(a.k);
@@ -143,19 +149,15 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   constexpr int QREGS = BF ? 4 : 32;
   typename std::conditional<BF, bf16x8, float>::type qf[QREGS];
   if constexpr (BF) {
-    const T* qrow = Qg + rowbase + (int64_t)mq * mstride + 8 * hh;
+    const T* qrow = Qg + rowbase + (int64_t)mqc * mstride + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 x = {0, 0, 0, 0};
-      if (qvalid) x = *reinterpret_cast<const u32x4*>(qrow + 16 * ks);
-      qf[ks] = __builtin_bit_cast(bf16x8, x);
-    }
+    for (int ks = 0; ks < 4; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * ks));
   } else {
-    const T* qrow = Qg + rowbase + (int64_t)mq * mstride;
+    const T* qrow = Qg + rowbase + (int64_t)mqc * mstride;
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (qvalid) x = *reinterpret_cast<const f32x4*>(qrow + 4 * c);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 4 * c);
       qf[2 * c] = hh ? x[1] : x[0];
       qf[2 * c + 1] = hh ? x[3] : x[2];
     }
@@ -176,11 +178,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       const int c = tid + i * NT;
       const int row = BF ? (c >> 3) : (c >> 4);
       const int ch = BF ? (c & 7) : (c & 15);
-      const int32_t m = mbase + row;
-      u32x4 x = {0, 0, 0, 0};
-      if (m < L) x = *reinterpret_cast<const u32x4*>(Kg + rowbase + (int64_t)m * mstride +
-                                                      ch * (BF ? 8 : 4));
-      kreg[i] = x;
+      const int32_t m = min(mbase + row, L - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(Kg + rowbase + (int64_t)m * mstride +
+                                                 ch * (BF ? 8 : 4));
     }
     if constexpr (BF) {
 #pragma unroll
@@ -189,11 +189,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
         const int kg = c >> 4, dg = c & 15;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int32_t m = mbase + 4 * kg + j;
-          u32x2 x = {0, 0};
-          if (m < L)
-            x = *reinterpret_cast<const u32x2*>(Vg + rowbase + (int64_t)m * mstride + 4 * dg);
-          vreg[i][j] = x;
+          const int32_t m = min(mbase + 4 * kg + j, L - 1);
+          vreg[i][j] =
+              *reinterpret_cast<const u32x2*>(Vg + rowbase + (int64_t)m * mstride + 4 * dg);
         }
       }
     } else {
@@ -201,11 +199,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       for (int i = 0; i < CV; ++i) {
         const int c = tid + i * NT;
         const int row = c >> 4, ch = c & 15;
-        const int32_t m = mbase + row;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
-        if (m < L)
-          x = *reinterpret_cast<const f32x4*>(Vg + rowbase + (int64_t)m * mstride + 4 * ch);
-        vreg32[i] = x;
+        const int32_t m = min(mbase + row, L - 1);
+        vreg32[i] = *reinterpret_cast<const f32x4*>(Vg + rowbase + (int64_t)m * mstride + 4 * ch);
       }
     }
   };
@@ -308,9 +303,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
     mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = exp2_fast(m_run - m_new);
-    m_run = m_new;
+    // Lazy rescaling: the running max (log2 domain) only moves when some row
+    // of the wave gains more than 8, so p = 2^(s - m_run) stays below 2^8
+    // and most tiles skip rescaling O and l.
+    const float mt = mx * sl2;
+    if (__ballot(mt > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) O[db] *= alpha;
+    }
 
     float lsum = 0.f;
     if constexpr (BF) {
@@ -319,8 +323,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e], sl2, -m_new));
-          const float p1 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e + 1], sl2, -m_new));
+          const float p0 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e], sl2, -m_run));
+          const float p1 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e + 1], sl2, -m_run));
           bf16x2 pr;
           pr[0] = (__bf16)p0;
           pr[1] = (__bf16)p1;
@@ -330,9 +334,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
           lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
         }
       }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) O[db] *= alpha;
+      l_run += lsum;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const T* Vr = V + (db * 32 + n) * SM::kVtStride + 4 * hh;
@@ -350,12 +352,10 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          pf[kb][v] = exp2_fast(fmaf(S[kb][v], sl2, -m_new));
+          pf[kb][v] = exp2_fast(fmaf(S[kb][v], sl2, -m_run));
           lsum += pf[kb][v];
         }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) O[db] *= alpha;
+      l_run += lsum;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll

@@ -52,9 +52,15 @@ struct PatDev {
   FastDiv r_div;   // division by r
 };
 
-// Attention launch. Tiles of all patterns share one grid; patterns are
-// stored sorted by ntile (descending) so that block ids can be handed out
-// heaviest tile first (see decode_tile).
+// Attention launch. Tiles of all patterns share one grid. Block ids are
+// dealt to the chip's XCDs round-robin (id mod kXcds), so the tiles are laid
+// out per XCD: each XCD walks its own list of (batch, head, segment) units,
+// all query tiles of a unit next to each other, heaviest (last) tile first.
+// Tiles of one unit then run at the same time on one XCD and read the same
+// key/value rows through that XCD's L2. Patterns are stored sorted by ntile
+// (descending); units are handed to XCDs round-robin in that order.
+constexpr int kXcds = 8;
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -69,8 +75,7 @@ struct AttnArgs {
   float sl2;       // softmax scale * log2(e)
   int32_t pad_;
   PatDev pat[kMaxPat];
-  int64_t unit_prefix[kMaxPat + 1];  // prefix sums of units in sorted order
-  int64_t band_start[kMaxPat + 1];   // first block id of each band (see decode_tile)
+  int64_t unit_start[kMaxPat + 1];  // first global unit of each sorted pattern
 };
 
 struct MergeArgs {

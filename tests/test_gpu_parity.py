@@ -7,9 +7,11 @@ pre-filled with NaN so an element the kernels never write fails the check.
 
 Log-sum-exp tolerance (no figure is given for it, so it is derived): the bf16
 kernel sums the bf16-rounded probabilities it feeds to the PV product, so its
-row sum carries each term's relative rounding error, at most 2^-9, and ln of
-the sum is off by at most about 2^-9 = 1.95e-3; fp32 score rounding adds far
-less. Hence 2.5e-3 for bf16 and 1e-4 for fp32.
+row sum carries each term's relative rounding error, at most the bf16 unit
+roundoff u = 2^-8 (8-bit significand, round to nearest even), and ln of the
+sum is off by at most about u = 3.9e-3. Scores are accumulated in fp32
+(relative error ~2^-24 of sum |q_d k_d|) and exp2/log2 add ~1e-6, so 4e-3
+for bf16. The fp32 kernel keeps probabilities in fp32: 1e-4.
 """
 import math
 
@@ -23,7 +25,7 @@ from sparse_long_sequence_attn_amd.workloads import (WORKLOADS, device_inputs, f
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 2.5e-3)}
+TOL = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 4e-3)}
 
 
 @pytest.fixture(scope="module")
