@@ -65,7 +65,10 @@ enum {
   DA_OK = 0,
   DA_ERR_NULL = -1,      /* a required pointer is NULL                          */
   DA_ERR_SHAPE = -2,     /* B, N or H negative, N not a multiple of min(w, N),  */
-                         /* or sizes beyond the supported range                 */
+                         /* or sizes beyond the supported range: N * H and     */
+                         /* B below 2^31 and 2^16, and one segment plus 128    */
+                         /* dilated rows, (min(w,N) + 128 r) * H * Dh * element */
+                         /* size, below 2^31 bytes                             */
   DA_ERR_PATTERN = -3,   /* n_patterns outside 1..DA_MAX_PATTERNS, w < 1,       */
                          /* r < 1 or r > min(w, N)                              */
   DA_ERR_DTYPE = -4,     /* dtype is not DA_F32 or DA_BF16                      */

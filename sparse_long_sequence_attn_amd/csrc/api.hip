@@ -60,6 +60,10 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
       const int64_t wp = std::min<int64_t>(patterns[i].w, N);
       if (N % wp != 0) return DA_ERR_SHAPE;
       if (patterns[i].r > wp) return DA_ERR_PATTERN;
+      // the attention kernel addresses one segment's rows with 32-bit byte
+      // offsets (plus at most one 128-row tile of overrun)
+      const int64_t esize = dtype == DA_BF16 ? 2 : 4;
+      if ((wp + 128 * (int64_t)patterns[i].r) * H * Dh * esize > kMaxGrid) return DA_ERR_SHAPE;
     }
   }
   pl->bf16 = dtype == DA_BF16;
@@ -90,7 +94,7 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
   }
   // one 32-row wave per workgroup when every segment is that short
   pl->nw = lmax_all > 32 ? 4 : 1;
-  const int bm = da::attn_tile_rows(pl->nw);
+  const int bm = da::attn_tile_rows(pl->bf16, pl->nw);
   for (int i = 0; i < n_patterns; ++i) pl->pat[i].ntile = (pl->pat[i].lmax + bm - 1) / bm;
 
   for (int i = 0; i < n_patterns; ++i) pl->order[i] = i;

@@ -11,8 +11,11 @@
 // Work decomposition (NW waves of 64 lanes per workgroup):
 //   * each wave owns 32 query rows (BM = 32 * NW per workgroup);
 //   * key/value tiles of BN gathered rows are staged through LDS, double
-//     buffered, loaded by the whole workgroup: K row-major with a 16-byte
-//     XOR swizzle, V transposed (d-major) so PV operands are contiguous;
+//     buffered, loaded by the whole workgroup with buffer loads whose
+//     hardware range check returns zeros for rows past the segment's last
+//     gathered row; K is stored row-major with a 16-byte XOR swizzle, V
+//     row-major with padded rows, and the PV operand (4 keys of one head
+//     dimension per lane) is fetched with the LDS transpose read;
 //   * S^T = K Q^T and O^T += V^T P^T run on MFMA 32x32 blocks. With S^T, a
 //     lane holds one query and 16 keys of a block, so row max and row sum
 //     are in-lane except for one exchange with the lane 32 apart.
@@ -74,6 +77,28 @@ __device__ inline bool decode_tile(const AttnArgs& a, int64_t id, Tile* t) {
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer over [base, base + bytes): 16-byte loads at 32-bit offsets;
+// offsets at or past `bytes` read as zero (gfx9 resource word 3 = 0x00020000).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane m supplies 4 consecutive 16-bit elements; view them in lane order as
+// a 4 x 16 matrix (rows = lanes 4j..4j+3). Lane i receives column i:
+// element j = row j, column i.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+__device__ inline u32x2 lds_read_tr16(const char __attribute__((address_space(3))) * base,
+                                      uint32_t byte_off) {
+  return __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(base + byte_off)));
+}
+
 // Combine a per-lane value with the lane 32 apart (both halves of a query).
 __device__ inline float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -84,21 +109,24 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool BF, int NW, int BN>
+template <bool BF, int BN>
 struct Smem {
-  // bf16: K [BN][64] swizzled, V^T [64][BN + 4]; fp32: K [BN][65], V [BN][64]
-  static constexpr int kVtStride = BN + 4;
+  // bf16: K [BN][64] swizzled, V [BN][72] (144-byte rows); fp32: K [BN][65], V [BN][64]
+  static constexpr int kVStride = BF ? kDh + 8 : kDh;
   static constexpr int kKElems = BF ? BN * kDh : BN * (kDh + 1);
-  static constexpr int kVElems = BF ? kDh * kVtStride : BN * kDh;
+  static constexpr int kVElems = BN * kVStride;
   static constexpr int kElemBytes = BF ? 2 : 4;
   static constexpr int kBytes = 2 * (kKElems + kVElems) * kElemBytes;
 };
 
-template <int NW, int BN, bool CAUSAL, bool FINAL, bool BF>
+// NW waves per workgroup, each owning QB blocks of 32 query rows (so every
+// K and V fragment read from LDS feeds QB MFMAs); BN keys per LDS tile.
+template <int NW, int QB, int BN, bool CAUSAL, bool FINAL, bool BF>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   using T = typename std::conditional<BF, __bf16, float>::type;
-  using SM = Smem<BF, NW, BN>;
-  constexpr int BM = 32 * NW;
+  using SM = Smem<BF, BN>;
+  constexpr int QW = 32 * QB;  // query rows per wave
+  constexpr int BM = QW * NW;  // query rows per workgroup
   constexpr int NT = 64 * NW;
   constexpr int KB = BN / 32;
   static_assert(BN % 32 == 0 && BN <= 128, "key tile");
@@ -132,155 +160,137 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
 
   const int32_t qend_wg = min(L, q0 + BM);
   const int32_t nkt = CAUSAL ? (qend_wg + BN - 1) / BN : (L + BN - 1) / BN;
-  const int32_t qw0 = q0 + wv * 32;
-  const int32_t qend_w = min(L, qw0 + 32);
+  const int32_t qw0 = q0 + wv * QW;
+  const int32_t qend_w = min(L, qw0 + QW);
   const int32_t nkt_w = qw0 >= L ? 0 : (CAUSAL ? (qend_w + BN - 1) / BN : nkt);
-  const int32_t mq = qw0 + n;  // this lane's query (gathered index)
-  const bool qvalid = mq < L;
-  // Rows past L are read from row L-1 instead of being skipped: keys past L
-  // are masked and queries past L are never stored, so no load needs a branch.
-  const int32_t mqc = min(mq, L - 1);
+  int32_t mq[QB];  // this lane's queries (gathered indices)
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mq[qb] = qw0 + 32 * qb + n;
 
-  const T* const Qg = reinterpret_cast<const T*>(a.q);
-  const T* const Kg = reinterpret_cast<const T*>(a.k);
-  const T* const Vg = reinterpret_cast<const T*>(a.v);
+  // Buffers over this segment's gathered rows: row m at byte m * mbytes.
+  // Rows past L fall outside the range and load as zeros (such keys are
+  // masked and such queries are never stored). The host keeps these
+  // offsets below 2^31.
+  constexpr uint32_t kRowBytes = kDh * sizeof(T);
+  const uint32_t mbytes = (uint32_t)(mstride * sizeof(T));
+  const uint32_t range = (uint32_t)(L - 1) * mbytes + kRowBytes;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const T*>(a.q) + rowbase, range);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const T*>(a.k) + rowbase, range);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, range);
 
   // ---- query fragments (B operand of S^T = K Q^T), kept in registers
   constexpr int QREGS = BF ? 4 : 32;
-  typename std::conditional<BF, bf16x8, float>::type qf[QREGS];
-  if constexpr (BF) {
-    const T* qrow = Qg + rowbase + (int64_t)mqc * mstride + 8 * hh;
+  typename std::conditional<BF, bf16x8, float>::type qf[QB][QREGS];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * ks));
-  } else {
-    const T* qrow = Qg + rowbase + (int64_t)mqc * mstride;
+  for (int qb = 0; qb < QB; ++qb) {
+    const uint32_t qoff = (uint32_t)mq[qb] * mbytes;
+    if constexpr (BF) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(qrow + 4 * c);
-      qf[2 * c] = hh ? x[1] : x[0];
-      qf[2 * c + 1] = hh ? x[3] : x[2];
+      for (int ks = 0; ks < 4; ++ks)
+        qf[qb][ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, qoff + (16 * ks + 8 * hh) * 2));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const f32x4 x = __builtin_bit_cast(f32x4, buf_load16(rq, qoff + 16 * c));
+        qf[qb][2 * c] = hh ? x[1] : x[0];
+        qf[qb][2 * c + 1] = hh ? x[3] : x[2];
+      }
     }
   }
 
-  // ---- key/value tile staging: global -> registers -> LDS
-  constexpr int CK = BF ? BN * 8 / NT : BN * 16 / NT;  // 16-byte K chunks per thread
-  constexpr int CV = BF ? BN * 4 / NT : BN * 16 / NT;  // V items per thread
-  static_assert(CK >= 1 && CV >= 1, "tile too small for the workgroup");
-  u32x4 kreg[CK];
-  u32x2 vreg[BF ? CV : 1][4];
-  f32x4 vreg32[BF ? 1 : CV];
+  // ---- key/value tile staging: global -> registers -> LDS. Thread chunk c
+  // of a tile is 16 bytes of row c / (row bytes / 16); K and V share offsets.
+  constexpr int kChunksPerRow = kRowBytes / 16;  // 8 (bf16) or 16 (fp32)
+  constexpr int CK = BN * kChunksPerRow / NT;     // chunks per thread per tensor
+  static_assert(CK >= 1 && BN * kChunksPerRow % NT == 0, "tile too small for the workgroup");
+  u32x4 kreg[CK], vreg[CK];
+  uint32_t koff[CK];
+#pragma unroll
+  for (int i = 0; i < CK; ++i) {
+    const int c = tid + i * NT;
+    koff[i] = (uint32_t)(c / kChunksPerRow) * mbytes + (uint32_t)(c % kChunksPerRow) * 16;
+  }
+  const uint32_t tile_bytes = (uint32_t)BN * mbytes;
 
   auto load_tile = [&](int kt) {
-    const int32_t mbase = kt * BN;
+    const uint32_t base = (uint32_t)kt * tile_bytes;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
-      const int c = tid + i * NT;
-      const int row = BF ? (c >> 3) : (c >> 4);
-      const int ch = BF ? (c & 7) : (c & 15);
-      const int32_t m = min(mbase + row, L - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(Kg + rowbase + (int64_t)m * mstride +
-                                                 ch * (BF ? 8 : 4));
-    }
-    if constexpr (BF) {
-#pragma unroll
-      for (int i = 0; i < CV; ++i) {
-        const int c = tid + i * NT;
-        const int kg = c >> 4, dg = c & 15;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int32_t m = min(mbase + 4 * kg + j, L - 1);
-          vreg[i][j] =
-              *reinterpret_cast<const u32x2*>(Vg + rowbase + (int64_t)m * mstride + 4 * dg);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CV; ++i) {
-        const int c = tid + i * NT;
-        const int row = c >> 4, ch = c & 15;
-        const int32_t m = min(mbase + row, L - 1);
-        vreg32[i] = *reinterpret_cast<const f32x4*>(Vg + rowbase + (int64_t)m * mstride + 4 * ch);
-      }
+      kreg[i] = buf_load16(rk, base + koff[i]);
+      vreg[i] = buf_load16(rv, base + koff[i]);
     }
   };
 
+  // K rows: 16-byte chunk j of row x goes to slot j ^ ((x >> 1) & 7), so the
+  // 16 lanes the LDS serves together (rows x..x+15, one chunk index each)
+  // hit 16 distinct 16-byte bank groups of the 256-byte bank window.
   auto store_tile = [&](int buf) {
     T* K = Ks + buf * SM::kKElems;
     T* V = Vs + buf * SM::kVElems;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * NT;
+      const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
       if constexpr (BF) {
-        const int row = c >> 3, ch = c & 7;
-        *reinterpret_cast<u32x4*>(K + row * kDh + ((ch ^ (row & 7)) << 3)) = kreg[i];
+        *reinterpret_cast<u32x4*>(K + row * kDh + ((ch ^ ((row >> 1) & 7)) << 3)) = kreg[i];
+        *reinterpret_cast<u32x4*>(V + row * SM::kVStride + ch * 8) = vreg[i];
       } else {
-        const int row = c >> 4, ch = c & 15;
         float* dst = reinterpret_cast<float*>(K) + row * (kDh + 1) + 4 * ch;
 #pragma unroll
         for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(kreg[i][e]);
-      }
-    }
-    if constexpr (BF) {
-      // 4 keys x 4 dims -> 4 dims x 4 keys (bf16 pairs regrouped)
-#pragma unroll
-      for (int i = 0; i < CV; ++i) {
-        const int c = tid + i * NT;
-        const int kg = c >> 4, dg = c & 15;
-        const u32x2* x = vreg[i];
-        u32x2 o[4];
-        o[0] = u32x2{(x[0][0] & 0xffffu) | (x[1][0] << 16), (x[2][0] & 0xffffu) | (x[3][0] << 16)};
-        o[1] = u32x2{(x[0][0] >> 16) | (x[1][0] & 0xffff0000u),
-                     (x[2][0] >> 16) | (x[3][0] & 0xffff0000u)};
-        o[2] = u32x2{(x[0][1] & 0xffffu) | (x[1][1] << 16), (x[2][1] & 0xffffu) | (x[3][1] << 16)};
-        o[3] = u32x2{(x[0][1] >> 16) | (x[1][1] & 0xffff0000u),
-                     (x[2][1] >> 16) | (x[3][1] & 0xffff0000u)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *reinterpret_cast<u32x2*>(V + (4 * dg + e) * SM::kVtStride + 4 * kg) = o[e];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < CV; ++i) {
-        const int c = tid + i * NT;
-        const int row = c >> 4, ch = c & 15;
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(V) + row * kDh + 4 * ch) = vreg32[i];
+        *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(V) + row * kDh + 4 * ch) = vreg[i];
       }
     }
   };
 
-  // ---- running state: O^T accumulators (2 blocks of 32 dims), row max
-  // (log2 domain, identical in both lane halves) and this half's row sum
-  f32x16 O[2];
+  // ---- running state per query block: O^T accumulators (2 blocks of 32
+  // dims), row max (log2 domain, identical in both lane halves) and this
+  // half's row sum
+  f32x16 O[2][QB];
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) O[db][v] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[db][qb][v] = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
   const float sl2 = a.sl2;
+  const int m16 = lane & 15, g16 = lane >> 4;
 
   auto compute = [&](int buf, int kt) {
     const T* K = Ks + buf * SM::kKElems;
     const T* V = Vs + buf * SM::kVElems;
-    f32x16 S[KB];
+    f32x16 S[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) S[kb][v] = 0.f;
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[kb][qb][v] = 0.f;
       const int row = kb * 32 + n;
       if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              K + row * kDh + (((2 * ks + hh) ^ (n & 7)) << 3));
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kb], 0, 0, 0);
+              K + row * kDh + (((2 * ks + hh) ^ ((row >> 1) & 7)) << 3));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], S[kb][qb], 0, 0, 0);
         }
       } else {
         const float* Kr = reinterpret_cast<const float*>(K) + row * (kDh + 1) + hh;
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks)
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(Kr[2 * ks], qf[ks], S[kb], 0, 0, 0);
+        for (int ks = 0; ks < 32; ++ks) {
+          const float kv = Kr[2 * ks];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            S[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, qf[qb][ks], S[kb][qb], 0, 0, 0);
+        }
       }
     }
 
@@ -292,70 +302,100 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int32_t key = kt * BN + kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          const bool dead = CAUSAL ? (key > mq) : (key >= L);
-          if (dead) S[kb][v] = -INFINITY;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const bool dead = CAUSAL ? (key > mq[qb]) : (key >= L);
+            if (dead) S[kb][qb][v] = -INFINITY;
+          }
         }
     }
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
-    mx = pair_max(mx);
-    // Lazy rescaling: the running max (log2 domain) only moves when some row
-    // of the wave gains more than 8, so p = 2^(s - m_run) stays below 2^8
+    // Lazy rescaling: a row's running max (log2 domain) only moves when the
+    // tile raises it by more than 8, so p = 2^(s - m_run) stays below 2^8
     // and most tiles skip rescaling O and l.
-    const float mt = mx * sl2;
-    if (__ballot(mt > m_run + 8.f) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2_fast(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    float mt[QB];
+    bool grow = false;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) O[db] *= alpha;
-    }
-
-    float lsum = 0.f;
-    if constexpr (BF) {
-      bf16x8 pb[2 * KB];
-#pragma unroll
-      for (int c = 0; c < 2 * KB; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e], sl2, -m_run));
-          const float p1 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e + 1], sl2, -m_run));
-          bf16x2 pr;
-          pr[0] = (__bf16)p0;
-          pr[1] = (__bf16)p1;
-          pb[c][e] = pr[0];
-          pb[c][e + 1] = pr[1];
-          const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
-        }
-      }
-      l_run += lsum;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const T* Vr = V + (db * 32 + n) * SM::kVtStride + 4 * hh;
-#pragma unroll
-        for (int c = 0; c < 2 * KB; ++c) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(Vr + 16 * c);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(Vr + 16 * c + 8);
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[c], O[db], 0, 0, 0);
-        }
-      }
-    } else {
-      float pf[KB][16];
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          pf[kb][v] = exp2_fast(fmaf(S[kb][v], sl2, -m_run));
-          lsum += pf[kb][v];
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][qb][v]);
+      mt[qb] = pair_max(mx) * sl2;
+      grow = grow || (mt[qb] > m_run[qb] + 8.f);
+    }
+    if (__ballot(grow) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m_run[qb], mt[qb]);
+        const float alpha = exp2_fast(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) O[db][qb] *= alpha;
+      }
+    }
+
+    if constexpr (BF) {
+      bf16x8 pb[QB][2 * KB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2 * KB; ++c) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = exp2_fast(fmaf(S[c >> 1][qb][8 * (c & 1) + e], sl2, -m_run[qb]));
+            const float p1 = exp2_fast(fmaf(S[c >> 1][qb][8 * (c & 1) + e + 1], sl2, -m_run[qb]));
+            bf16x2 pr;
+            pr[0] = (__bf16)p0;
+            pr[1] = (__bf16)p1;
+            pb[qb][c][e] = pr[0];
+            pb[qb][c][e + 1] = pr[1];
+            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
+          }
         }
-      l_run += lsum;
+        l_run[qb] += lsum;
+      }
+      // A operand of O^T += V^T P^T for (dims db*32.., keys 16c..16c+15):
+      // lane (n, hh) needs V[16c + 8h + 4hh + j][db*32 + n], j = 0..3, for
+      // h = 0, 1. In 16-lane group g (n = 16(g&1) + i, hh = g>>1) lane m
+      // points at row 16c + 8h + 4hh + m/4, dims db*32 + 16(g&1) + 4(m&3)..+3;
+      // the transpose read then hands lane i the four keys of dim i.
+      const char __attribute__((address_space(3)))* vbase =
+          (const char __attribute__((address_space(3)))*)smem +
+          (2 * SM::kKElems + buf * SM::kVElems) * sizeof(T);
+      const uint32_t vlane = (uint32_t)((4 * (g16 >> 1) + (m16 >> 2)) * SM::kVStride +
+                                        16 * (g16 & 1) + 4 * (m16 & 3)) * 2;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+#pragma unroll
+        for (int c = 0; c < 2 * KB; ++c) {
+          const uint32_t o0 = vlane + (uint32_t)((16 * c) * SM::kVStride + db * 32) * 2;
+          const u32x2 lo = lds_read_tr16(vbase, o0);
+          const u32x2 hi = lds_read_tr16(vbase, o0 + 8 * SM::kVStride * 2);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb][c], O[db][qb], 0, 0, 0);
+        }
+      }
+    } else {
+      float pf[QB][KB][16];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            pf[qb][kb][v] = exp2_fast(fmaf(S[kb][qb][v], sl2, -m_run[qb]));
+            lsum += pf[qb][kb][v];
+          }
+        l_run[qb] += lsum;
+      }
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -364,7 +404,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
           for (int v = 0; v < 16; ++v) {
             const int key = kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
             const float vv = reinterpret_cast<const float*>(V)[key * kDh + db * 32 + n];
-            O[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, pf[kb][v], O[db], 0, 0, 0);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv, pf[qb][kb][v], O[db][qb], 0, 0, 0);
           }
     }
   };
@@ -381,95 +423,105 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     __syncthreads();
   }
 
-  if (!qvalid) return;
-  const float l_tot = pair_sum(l_run);
-  const float inv = 1.f / l_tot;
-  const float lse2 = m_run + __log2f(l_tot);
-  const int64_t pos = gathered_pos(tl.seg, wp, off, r, mq);
-
-  if constexpr (FINAL) {
-    T* orow = reinterpret_cast<T*>(a.out) + headbase;
-    float* lse_row = a.lse + ((int64_t)tl.b * a.H + tl.h) * a.N;
-    auto put = [&](int64_t t, bool zero) {
-      T* dst = orow + t * rs + 4 * hh;
+  // ---- epilogue: normalise and write each valid query row
+  float l_tot[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l_tot[qb] = pair_sum(l_run[qb]);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    if (mq[qb] >= L) continue;
+    const float inv = 1.f / l_tot[qb];
+    const float lse2 = m_run[qb] + __log2f(l_tot[qb]);
+    const int64_t pos = gathered_pos(tl.seg, wp, off, r, mq[qb]);
+    if constexpr (FINAL) {
+      T* orow = reinterpret_cast<T*>(a.out) + headbase;
+      float* lse_row = a.lse + ((int64_t)tl.b * a.H + tl.h) * a.N;
+      auto put = [&](int64_t t, bool zero) {
+        T* dst = orow + t * rs + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d = db * 32 + 8 * g;
+            if constexpr (BF) {
+              bf16x2 x0, x1;
+              x0[0] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 0] * inv);
+              x0[1] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 1] * inv);
+              x1[0] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 2] * inv);
+              x1[1] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 3] * inv);
+              *reinterpret_cast<u32x2*>(dst + d) =
+                  u32x2{__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1)};
+            } else {
+              f32x4 x;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[e] = zero ? 0.f : O[db][qb][4 * g + e] * inv;
+              *reinterpret_cast<f32x4*>(dst + d) = x;
+            }
+          }
+        if (hh == 0) lse_row[t] = zero ? -INFINITY : lse2 * kLn2;
+      };
+      put(pos, false);
+      // positions of this segment that the head does not gather: the r-1
+      // after each gathered row and, before the first one, the offset rows
+      const int64_t seg_end = seg0 + wp;
+      for (int j = 1; j < r; ++j) {
+        if (pos + j >= seg_end) break;
+        put(pos + j, true);
+      }
+      if (mq[qb] == 0)
+        for (int j = 0; j < off; ++j) put(seg0 + j, true);
+    } else {
+      const int64_t prow = (((int64_t)tl.b * a.H + tl.h) * P.nseg + tl.seg) * P.lmax + mq[qb];
+      float* po = a.ws + P.po_off + prow * kDh + 4 * hh;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int d = db * 32 + 8 * g;
-          if constexpr (BF) {
-            bf16x2 x0, x1;
-            x0[0] = (__bf16)(zero ? 0.f : O[db][4 * g + 0] * inv);
-            x0[1] = (__bf16)(zero ? 0.f : O[db][4 * g + 1] * inv);
-            x1[0] = (__bf16)(zero ? 0.f : O[db][4 * g + 2] * inv);
-            x1[1] = (__bf16)(zero ? 0.f : O[db][4 * g + 3] * inv);
-            *reinterpret_cast<u32x2*>(dst + d) =
-                u32x2{__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1)};
-          } else {
-            f32x4 x;
+          f32x4 x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = zero ? 0.f : O[db][4 * g + e] * inv;
-            *reinterpret_cast<f32x4*>(dst + d) = x;
-          }
+          for (int e = 0; e < 4; ++e) x[e] = O[db][qb][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g) = x;
         }
-      if (hh == 0) lse_row[t] = zero ? -INFINITY : lse2 * kLn2;
-    };
-    put(pos, false);
-    // positions of this segment that the head does not gather: the r-1
-    // after each gathered row and, before the first one, the offset rows
-    const int64_t seg_end = seg0 + wp;
-    for (int j = 1; j < r; ++j) {
-      if (pos + j >= seg_end) break;
-      put(pos + j, true);
+      if (hh == 0) a.ws[P.pl_off + prow] = lse2;
     }
-    if (mq == 0)
-      for (int j = 0; j < off; ++j) put(seg0 + j, true);
-  } else {
-    const int64_t prow = (((int64_t)tl.b * a.H + tl.h) * P.nseg + tl.seg) * P.lmax + mq;
-    float* po = a.ws + P.po_off + prow * kDh + 4 * hh;
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = O[db][4 * g + e] * inv;
-        *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g) = x;
-      }
-    if (hh == 0) a.ws[P.pl_off + prow] = lse2;
   }
 }
 
-template <int NW, int BN, bool BF>
-hipError_t launch_nw(const AttnArgs& a, bool causal, bool final_out, int64_t grid,
-                     hipStream_t st) {
+template <int NW, int QB, int BN, bool BF>
+hipError_t launch_cfg(const AttnArgs& a, bool causal, bool final_out, int64_t grid,
+                      hipStream_t st) {
   dim3 g((uint32_t)grid), b(NW * 64);
   if (causal) {
     if (final_out)
-      hipLaunchKernelGGL((attn_fwd_kernel<NW, BN, true, true, BF>), g, b, 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NW, QB, BN, true, true, BF>), g, b, 0, st, a);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<NW, BN, true, false, BF>), g, b, 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NW, QB, BN, true, false, BF>), g, b, 0, st, a);
   } else {
     if (final_out)
-      hipLaunchKernelGGL((attn_fwd_kernel<NW, BN, false, true, BF>), g, b, 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NW, QB, BN, false, true, BF>), g, b, 0, st, a);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<NW, BN, false, false, BF>), g, b, 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_kernel<NW, QB, BN, false, false, BF>), g, b, 0, st, a);
   }
   return hipGetLastError();
 }
 
+// Launch shapes: bf16 long segments use 4 waves x 64 query rows with 64-key
+// tiles; fp32 (not the MFMA-rate path) 4 waves x 32 rows; segments of at
+// most 32 gathered rows use one 32-row wave per workgroup with 32-key tiles.
+constexpr int kQbBf16 = 1;
+
 }  // namespace
 
-int attn_tile_rows(int nw) { return 32 * nw; }
+int attn_tile_rows(bool bf16, int nw) { return nw == 4 ? 32 * nw * (bf16 ? kQbBf16 : 1) : 32; }
 
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, bool final_out,
                             int64_t grid, hipStream_t st) {
   if (bf16) {
-    if (nw == 4) return launch_nw<4, 64, true>(a, causal, final_out, grid, st);
-    return launch_nw<1, 32, true>(a, causal, final_out, grid, st);
+    if (nw == 4) return launch_cfg<4, kQbBf16, 64, true>(a, causal, final_out, grid, st);
+    return launch_cfg<1, 1, 32, true>(a, causal, final_out, grid, st);
   }
-  if (nw == 4) return launch_nw<4, 64, false>(a, causal, final_out, grid, st);
-  return launch_nw<1, 32, false>(a, causal, final_out, grid, st);
+  if (nw == 4) return launch_cfg<4, 1, 64, false>(a, causal, final_out, grid, st);
+  return launch_cfg<1, 1, 32, false>(a, causal, final_out, grid, st);
 }
 
 }  // namespace da

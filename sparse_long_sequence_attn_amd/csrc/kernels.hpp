@@ -6,11 +6,11 @@
 
 namespace da {
 
-// Query rows per attention workgroup for nw waves.
-int attn_tile_rows(int nw);
+// Query rows per attention workgroup for nw waves (4 or 1) and the dtype.
+int attn_tile_rows(bool bf16, int nw);
 
 // The fused gather / QK^T / online softmax / PV kernel over every tile of
-// every pattern in `a` (grid = total tiles). nw is 4 (128-row tiles, 64-key
+// every pattern in `a`. nw is 4 (256-row bf16 / 128-row fp32 tiles, 64-key
 // LDS tiles) or 1 (32-row tiles, 32-key LDS tiles, for short segments).
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, bool final_out,
                             int64_t grid, hipStream_t st);
