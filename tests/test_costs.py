@@ -1,0 +1,38 @@
+"""The work/traffic model used for reporting, against hand-derived counts."""
+import json
+import os
+
+from sparse_long_sequence_attn_amd.costs import cost
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_paper_mixture_flops_from_rows_per_head():
+    with open(os.path.join(GOLDEN, "paper_mixture_rows_per_head.json")) as f:
+        g = json.load(f)
+    N, H, Dh = g["N"], g["H"], 64
+    # causal segment of L rows: L(L+1)/2 (query, key) pairs, 4*Dh flops each
+    # (2*Dh for the score, 2*Dh for the weighted value sum)
+    alg = sum(p["nseg"] * 2 * Dh * L * (L + 1) for p in g["patterns"] for L in p["L"])
+    rows = sum(p["nseg"] * L for p in g["patterns"] for L in p["L"])
+    c = cost(1, N, H, Dh, [(p["w"], p["r"]) for p in g["patterns"]], True, 2)
+    assert c.flops_alg == alg
+    assert c.gathered_rows == rows
+    assert abs(c.flops_alg / 1e9 - 286.47) < 0.01
+    # spec formula: 4 N (w/r) Dh H per pattern, halved for causal
+    ns = sum(4 * N * (p["w"] / p["r"]) * Dh * H / 2 for p in g["patterns"])
+    assert abs(c.flops_ns - ns) < 1e-3 * ns
+
+
+def test_single_pattern_bytes():
+    # usage-example shape: half of q, k, v gathered (r = 2), out + lse written once
+    c = cost(32, 8192, 8, 64, [(64, 2)], True, 2)
+    half = 32 * 8192 * 8 * 64 * 2 // 2
+    assert c.attn_read_bytes == 3 * half
+    assert c.attn_write_bytes == 32 * 8192 * 8 * 64 * 2 + 32 * 8 * 8192 * 4
+    assert c.merge_bytes == 0
+
+
+def test_non_causal_pairs():
+    c = cost(1, 64, 2, 64, [(64, 1)], False, 4)
+    assert c.flops_alg == 2 * 64 * 4 * 64 * 64
