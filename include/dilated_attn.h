@@ -106,10 +106,13 @@ int dilated_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
  * time each kernel with events between them. Same arguments and checks as
  * dilated_attn_fwd; calling _attention then _merge on one stream with the
  * same arguments is exactly dilated_attn_fwd.
- *  _attention: one launch covering every pattern. With one pattern it writes
- *              out and lse; with more it writes the workspace partials.
- *  _merge:     combines the workspace partials into out and lse; does
- *              nothing for a single pattern. */
+ *  _attention: one launch covering every pattern. It writes out and lse for
+ *              every row that exactly one pattern gathers (with a single
+ *              pattern also 0 / -inf for the rows it does not gather), and
+ *              workspace partials for rows that several patterns gather.
+ *  _merge:     combines the workspace partials into out and lse for rows
+ *              two or more patterns gather, and writes 0 / -inf for rows no
+ *              pattern gathers; does nothing for a single pattern. */
 int dilated_attn_fwd_attention(const void* q, const void* k, const void* v, void* out, float* lse,
                                int64_t B, int64_t N, int32_t H, int32_t Dh,
                                const da_pattern* patterns, int32_t n_patterns, int32_t causal,

@@ -29,9 +29,15 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags. The attention kernel never produces NaN (masked
+# scores are -inf and every processed row has a finite maximum), so max
+# operations need no NaN canonicalisation.
+EXTRA = {"attn_kernel.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -261,17 +261,23 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
   }
   const float sl2 = a.sl2;
   const int m16 = lane & 15, g16 = lane >> 4;
+  bool started = false;  // a tile has set the running max (wave-uniform)
 
   auto compute = [&](int buf, int kt) {
     const T* K = Ks + buf * SM::kKElems;
     const T* V = Vs + buf * SM::kVElems;
+    // key blocks (32 keys) of this tile that some query of the wave sees;
+    // later blocks are skipped (their scores stay -inf, their PV is skipped)
+    const int32_t kend = CAUSAL ? qw0 + QW : L;
+    const int nkb = min(KB, (kend - kt * BN + 31) / 32);
     f32x16 S[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) S[kb][qb][v] = 0.f;
+        for (int v = 0; v < 16; ++v) S[kb][qb][v] = kb < nkb ? 0.f : -INFINITY;
+      if (kb >= nkb) continue;
       const int row = kb * 32 + n;
       if constexpr (BF) {
 #pragma unroll
@@ -294,20 +300,35 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       }
     }
 
-    // mask: keys after the query (causal) or past the segment's rows
-    const bool need_mask = CAUSAL ? (kt * BN + BN - 1 > qw0) : ((kt + 1) * BN > L);
-    if (need_mask) {
+    // mask: keys after the query (causal) or past the segment's rows. Key
+    // and query blocks are 32-aligned, so a causal block is before its query
+    // block (no mask), on its diagonal, or after it (all dead).
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb >= nkb) continue;
+      const int32_t kb0 = kt * BN + kb * 32;
+      if (CAUSAL) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int32_t key = kt * BN + kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        for (int qb = 0; qb < QB; ++qb) {
+          const int32_t qs = qw0 + 32 * qb;
+          if (kb0 == qs) {
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const bool dead = CAUSAL ? (key > mq[qb]) : (key >= L);
-            if (dead) S[kb][qb][v] = -INFINITY;
+            for (int v = 0; v < 16; ++v)
+              if (8 * (v >> 2) + (v & 3) > n - 4 * hh) S[kb][qb][v] = -INFINITY;
+          } else if (kb0 > qs) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[kb][qb][v] = -INFINITY;
           }
         }
+      } else if (kb0 + 32 > L) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int32_t key = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (key >= L) S[kb][qb][v] = -INFINITY;
+        }
+      }
     }
 
     // Lazy rescaling: a row's running max (log2 domain) only moves when the
@@ -325,7 +346,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       mt[qb] = pair_max(mx) * sl2;
       grow = grow || (mt[qb] > m_run[qb] + 8.f);
     }
-    if (__ballot(grow) != 0) {
+    if (!started) {
+      // first tile: O and l are still zero, only the max is set
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) m_run[qb] = mt[qb];
+      started = true;
+    } else if (__ballot(grow) != 0) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const float m_new = fmaxf(m_run[qb], mt[qb]);
@@ -373,6 +399,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
         for (int c = 0; c < 2 * KB; ++c) {
+          if (c >= 2 * nkb) break;
           const uint32_t o0 = vlane + (uint32_t)((16 * c) * SM::kVStride + db * 32) * 2;
           const u32x2 lo = lds_read_tr16(vbase, o0);
           const u32x2 hi = lds_read_tr16(vbase, o0 + 8 * SM::kVStride * 2);
@@ -430,10 +457,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     if (mq[qb] >= L) continue;
-    const float inv = 1.f / l_tot[qb];
+    const float inv = __builtin_amdgcn_rcpf(l_tot[qb]);
     const float lse2 = m_run[qb] + __log2f(l_tot[qb]);
     const int64_t pos = gathered_pos(tl.seg, wp, off, r, mq[qb]);
-    if constexpr (FINAL) {
+    // A row that no other pattern gathers is final here and is written to
+    // out / lse directly; rows several patterns gather go through the
+    // partial buffers and the merge kernel.
+    bool direct = FINAL;
+    if constexpr (!FINAL) {
+      int cover = 0;
+      for (int i = 0; i < a.np; ++i)
+        cover += compact_index((uint32_t)pos, a.pat[i], head_offset(tl.h, a.pat[i].r)) >= 0;
+      direct = cover == 1;
+    }
+    if (direct) {
       T* orow = reinterpret_cast<T*>(a.out) + headbase;
       float* lse_row = a.lse + ((int64_t)tl.b * a.H + tl.h) * a.N;
       auto put = [&](int64_t t, bool zero) {
@@ -461,15 +498,18 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
         if (hh == 0) lse_row[t] = zero ? -INFINITY : lse2 * kLn2;
       };
       put(pos, false);
-      // positions of this segment that the head does not gather: the r-1
-      // after each gathered row and, before the first one, the offset rows
-      const int64_t seg_end = seg0 + wp;
-      for (int j = 1; j < r; ++j) {
-        if (pos + j >= seg_end) break;
-        put(pos + j, true);
+      if constexpr (FINAL) {
+        // one pattern: positions of this segment that the head does not
+        // gather (the r-1 after each gathered row and, before the first
+        // one, the offset rows) get 0 and -inf here
+        const int64_t seg_end = seg0 + wp;
+        for (int j = 1; j < r; ++j) {
+          if (pos + j >= seg_end) break;
+          put(pos + j, true);
+        }
+        if (mq[qb] == 0)
+          for (int j = 0; j < off; ++j) put(seg0 + j, true);
       }
-      if (mq[qb] == 0)
-        for (int j = 0; j < off; ++j) put(seg0 + j, true);
     } else {
       const int64_t prow = (((int64_t)tl.b * a.H + tl.h) * P.nseg + tl.seg) * P.lmax + mq[qb];
       float* po = a.ws + P.po_off + prow * kDh + 4 * hh;

@@ -6,8 +6,11 @@
 // its weights; weighting by each pattern's softmax denominator is the
 // reading implemented here. Rows no pattern gathers get 0 and -inf.
 //
-// The partials hold log2-domain lse values. The kernel is bound by HBM
-// traffic: 16 lanes cooperate on one 64-wide row with 16-byte loads.
+// The partials hold log2-domain lse values. Rows gathered by exactly one
+// pattern are final after the attention kernel and are skipped here. The
+// kernel is bound by HBM traffic: 4 lanes cooperate on one 64-wide row, each
+// moving 64 contiguous bytes of every covering pattern's partial, so one
+// wave handles 16 rows and the per-row coverage tests are shared by 4 lanes.
 #include "da_common.hpp"
 #include "kernels.hpp"
 
@@ -15,62 +18,91 @@ namespace da {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kRowsPerBlock = 16;
+constexpr int kLanesPerRow = 4;
+constexpr int kDimsPerLane = kDh / kLanesPerRow;  // 16
+constexpr int kThreads = 256;
+constexpr int kRowsPerBlock = kThreads / kLanesPerRow;  // 64
+
+__device__ inline uint32_t pack_bf16(float x, float y) {
+  bf16x2 p;
+  p[0] = (__bf16)x;
+  p[1] = (__bf16)y;
+  return __builtin_bit_cast(uint32_t, p);
+}
 
 template <bool BF>
-__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a, const FastDiv h_div) {
+__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a, const FastDiv h_div) {
   // blockIdx.y = batch; rows of one batch are (t, h) pairs in output order
-  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
+  const int sub = threadIdx.x % kLanesPerRow;
   if (row >= (uint32_t)(a.N * a.H)) return;
   const uint32_t t = fdiv(row, h_div);
   const int32_t h = (int32_t)(row - t * (uint32_t)a.H);
   const int64_t b = blockIdx.y;
 
+  // rows exactly one pattern gathers were written by the attention kernel
+  int32_t ci[kMaxPat];
+  int cover = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPat; ++i) {
+    ci[i] = i < a.np ? (int32_t)compact_index(t, a.pat[i], head_offset(h, a.pat[i].r)) : -1;
+    cover += ci[i] >= 0;
+  }
+  if (cover == 1) return;
+
+  // one pass to find the largest lse, one to sum the weights and outputs
   float l[kMaxPat];
-  f32x4 o[kMaxPat];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < kMaxPat; ++i) {
     l[i] = -INFINITY;
-    o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (i < a.np) {
+    if (ci[i] >= 0) {
       const PatDev& P = a.pat[i];
-      const int64_t ci = compact_index(t, P, head_offset(h, P.r));
-      if (ci >= 0) {
-        const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci;
-        l[i] = a.ws[P.pl_off + prow];
-        o[i] = *reinterpret_cast<const f32x4*>(a.ws + P.po_off + prow * kDh + 4 * sub);
-        mx = fmaxf(mx, l[i]);
-      }
+      // rows of one batch hold fewer than 2^31 slots (N * H < 2^31)
+      const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
+      l[i] = a.ws[P.pl_off + prow];
+      mx = fmaxf(mx, l[i]);
     }
   }
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4] = {};
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxPat; ++i) s += exp2f(l[i] - mx);
-    const float lse2 = mx + log2f(s);
+    for (int i = 0; i < kMaxPat; ++i)
+      if (ci[i] >= 0) s += __builtin_amdgcn_exp2f(l[i] - mx);
+    const float lse2 = mx + __builtin_amdgcn_logf(s);
 #pragma unroll
-    for (int i = 0; i < kMaxPat; ++i) acc += exp2f(l[i] - lse2) * o[i];
+    for (int i = 0; i < kMaxPat; ++i) {
+      if (ci[i] < 0) continue;
+      const PatDev& P = a.pat[i];
+      const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
+      const f32x4* src =
+          reinterpret_cast<const f32x4*>(a.ws + P.po_off + prow * kDh + kDimsPerLane * sub);
+      const float wgt = __builtin_amdgcn_exp2f(l[i] - lse2);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += wgt * src[j];
+    }
     lse = lse2 * kLn2;
   }
   const int64_t orow = (b * a.N + t) * a.H + h;
   if constexpr (BF) {
-    bf16x2 x0, x1;
-    x0[0] = (__bf16)acc[0];
-    x0[1] = (__bf16)acc[1];
-    x1[0] = (__bf16)acc[2];
-    x1[1] = (__bf16)acc[3];
-    *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(a.out) + orow * kDh + 4 * sub) =
-        u32x2{__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1)};
+    u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(a.out) + orow * kDh +
+                                          kDimsPerLane * sub);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      dst[j] = u32x4{pack_bf16(acc[2 * j][0], acc[2 * j][1]), pack_bf16(acc[2 * j][2], acc[2 * j][3]),
+                     pack_bf16(acc[2 * j + 1][0], acc[2 * j + 1][1]),
+                     pack_bf16(acc[2 * j + 1][2], acc[2 * j + 1][3])};
   } else {
-    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + orow * kDh + 4 * sub) = acc;
+    f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + orow * kDh +
+                                          kDimsPerLane * sub);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = acc[j];
   }
   if (sub == 0) a.lse[(b * a.H + h) * a.N + t] = lse;
 }
@@ -94,7 +126,7 @@ __global__ void coverage_map_kernel(const PatDev p, int32_t h, int64_t N, int64_
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = a.N * a.H;
-  dim3 g((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B), b(256);
+  dim3 g((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B), b(kThreads);
   const FastDiv hd = make_fastdiv((uint32_t)a.H);
   if (bf16)
     hipLaunchKernelGGL(merge_kernel<true>, g, b, 0, st, a, hd);
