@@ -12,11 +12,17 @@ h mod r, L = ceil((w' - off) / r) gathered rows per head and segment):
   query of every pattern, r times the rows a head gathers, so it exceeds the
   algorithmic count by about r for each pattern.
 * bytes: each kernel's compulsory HBM traffic - gathered q, k, v rows read
-  once, outputs and partials written once, partials read once by the merge.
+  once. A row that exactly one pattern gathers is written once as output by
+  the attention kernel; a row several patterns gather is written once per
+  covering pattern as an fp32 partial (Dh floats + lse), read back once by
+  the merge kernel, which also writes its output; a row no pattern gathers
+  is written (zeros) by the merge kernel.
 """
 import math
 from dataclasses import dataclass
 from typing import List, Sequence, Tuple
+
+import numpy as np
 
 Pattern = Tuple[int, int]
 
@@ -70,15 +76,27 @@ def cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causal: b
     for (w, r) in patterns:
         wp = min(w, N)
         flops_ns += B * 4.0 * N * (wp / r) * Dh * H * (0.5 if causal else 1.0)
-    out_bytes = B * N * H * Dh * elem_bytes + B * H * N * 4
+    out_row = Dh * elem_bytes + 4  # output row + its lse
+    part_row = (Dh + 1) * 4.0        # fp32 partial row + its lse
     attn_read = 3.0 * rows * Dh * elem_bytes
     if len(patterns) == 1:
-        attn_write = float(out_bytes)
+        attn_write = float(B * N * H * out_row)
         merge_read = merge_write = 0.0
     else:
-        attn_write = rows * (Dh + 1) * 4.0
-        merge_read = attn_write
-        merge_write = float(out_bytes)
+        single = multi_slots = multi_rows = none = 0
+        t = np.arange(N, dtype=np.int64)
+        for h in range(H):
+            count = np.zeros(N, dtype=np.int64)
+            for (w, r) in patterns:
+                wp = min(w, N)
+                count += ((t % wp) % r) == (h % r)
+            single += int((count == 1).sum())
+            none += int((count == 0).sum())
+            multi_rows += int((count >= 2).sum())
+            multi_slots += int(count[count >= 2].sum())
+        attn_write = B * (single * out_row + multi_slots * part_row)
+        merge_read = B * multi_slots * part_row
+        merge_write = B * (multi_rows + none) * float(out_row)
     return Cost(flops_alg, flops_ns, exps, rows, attn_read, attn_write, merge_read, merge_write)
 
 

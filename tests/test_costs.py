@@ -36,3 +36,14 @@ def test_single_pattern_bytes():
 def test_non_causal_pairs():
     c = cost(1, 64, 2, 64, [(64, 1)], False, 4)
     assert c.flops_alg == 2 * 64 * 4 * 64 * 64
+
+
+def test_merge_traffic_split():
+    # patterns (4, 1) and (8, 2) at N = 16, one head (offset 0): even
+    # positions are gathered by both patterns, odd ones by the first only
+    c = cost(1, 16, 1, 64, [(4, 1), (8, 2)], True, 2)
+    assert c.gathered_rows == 16 + 8
+    out_row, part_row = 64 * 2 + 4, 65 * 4
+    assert c.attn_write_bytes == 8 * out_row + 16 * part_row
+    assert c.merge_read_bytes == 16 * part_row
+    assert c.merge_write_bytes == 8 * out_row
