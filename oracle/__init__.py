@@ -42,6 +42,10 @@ def _bind(path):
         g.argtypes = [P, P, P, ctypes.c_int, i64, i64, i32, i32, P, i32, i32,
                       ctypes.c_double, ctypes.c_int, P, i64, P, P, P]
         g.restype = ctypes.c_int
+        bw = getattr(lib, "orc_bwd_" + sfx)
+        bw.argtypes = [P, P, P, P, ctypes.c_int, i64, i64, i32, i32, P, i32, i32,
+                       ctypes.c_double, ctypes.c_int, P, P, P]
+        bw.restype = ctypes.c_int
     return lib
 
 
@@ -158,6 +162,22 @@ class Oracle:
             return out, lse, pl
         return out, lse
 
+    def bwd(self, q, k, v, dout, patterns, causal=True, scale=None, precision="f64", threads=0):
+        """Gradients (dq, dk, dv) of sum(dout * out), each [B, N, H, Dh]."""
+        _check_inputs(q, k, v)
+        _check_inputs(q, dout, dout)
+        lib = self._lib
+        B, N, H, Dh = q.shape
+        real = np.float64 if precision == "f64" else np.float32
+        fn = lib.orc_bwd_f64 if precision == "f64" else lib.orc_bwd_f32
+        dq, dk, dv = (np.empty((B, N, H, Dh), dtype=real) for _ in range(3))
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _in_dtype(q), B, N, H, Dh,
+                _patterns(patterns), len(patterns), 1 if causal else 0, float(scale or 0.0),
+                int(threads), _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc:
+            raise RuntimeError(f"orc_bwd_{precision} -> {rc}")
+        return dq, dk, dv
+
 
 _default = None
 
@@ -187,3 +207,7 @@ def fwd(*args, **kwargs):
 
 def rows(*args, **kwargs):
     return default().rows(*args, **kwargs)
+
+
+def bwd(*args, **kwargs):
+    return default().bwd(*args, **kwargs)

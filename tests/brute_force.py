@@ -44,3 +44,30 @@ def union_softmax(q, k, v, patterns, causal=True, scale=None):
                 lse[b, h, t] = mx + math.log(e.sum())
                 out[b, t, h, :] = (e[:, None] * v[b, kk, h, :]).sum(0) / e.sum()
     return out, lse
+
+
+def union_softmax_torch(q, k, v, patterns, causal=True, scale=None):
+    """The same union softmax on torch float64 tensors [B, N, H, Dh], built
+    from differentiable torch ops only, so torch's autograd gives the exact
+    gradients of the definition (tiny inputs: one Python loop per row)."""
+    import torch
+
+    B, N, H, Dh = q.shape
+    sc = scale if scale else 1.0 / math.sqrt(Dh)
+    rows = []
+    for b in range(B):
+        for t in range(N):
+            for h in range(H):
+                keys = []
+                for (w, r) in patterns:
+                    pos = sparsified_positions(N, w, r, h, t)
+                    if pos is None:
+                        continue
+                    keys.extend(int(p) for p in pos if (not causal) or p <= t)
+                if not keys:
+                    rows.append(torch.zeros(Dh, dtype=q.dtype))
+                    continue
+                kk = torch.tensor(keys)
+                s = sc * (k[b, kk, h, :] @ q[b, t, h, :])
+                rows.append(torch.softmax(s, dim=0) @ v[b, kk, h, :])
+    return torch.stack(rows).reshape(B, N, H, Dh)

@@ -17,6 +17,7 @@ import torch
 
 import oracle
 from tests.brute_force import union_softmax
+from tests.mutants import build_mutant, pins_catching
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -423,25 +424,7 @@ PIN_SUITE = [
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m[3] for m in MUTANTS])
 def test_planted_mistakes_are_caught(tmp_path, mutant):
-    import shutil
-    import subprocess
-
     fname, old, new, _ = mutant
-    src_dir = os.path.dirname(oracle.__file__)
-    for f in ("dilated_oracle.c", "oracle_core.inc"):
-        shutil.copy(os.path.join(src_dir, f), tmp_path / f)
-    text = (tmp_path / fname).read_text()
-    assert text.count(old) >= 1, f"mutation site not found: {old!r}"
-    (tmp_path / fname).write_text(text.replace(old, new))
-    lib = tmp_path / "libmutant.so"
-    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", str(lib),
-                    str(tmp_path / "dilated_oracle.c"), "-lm"], check=True)
-    mut = oracle.Oracle(str(lib))
-    caught = []
-    with np.errstate(all="ignore"):
-        for pin in PIN_SUITE:
-            try:
-                pin(mut)
-            except (AssertionError, ValueError, RuntimeError):
-                caught.append(pin.__name__)
-    assert caught, "no pin rejects this planted mistake"
+    lib = build_mutant(tmp_path, fname, old, new)
+    assert pins_catching(lib, "tests.test_oracle_pins", "PIN_SUITE"), \
+        "no pin rejects this planted mistake"
