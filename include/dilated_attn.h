@@ -1,5 +1,6 @@
 /*
- * dilated_attn.h — C ABI of the MI355X (gfx950) dilated-attention forward pass.
+ * dilated_attn.h — C ABI of the MI355X (gfx950) dilated-attention forward and
+ * backward passes.
  *
  * The operation (sources: "LONGNET: Scaling Transformer to 1 billion tokens"
  * blog, sections "LongNet's attention allocation principle" and the
@@ -123,6 +124,61 @@ int dilated_attn_fwd_merge(const void* q, const void* k, const void* v, void* ou
                            const da_pattern* patterns, int32_t n_patterns, int32_t causal,
                            int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* ------------------------------------------------------------------ backward
+ *
+ * Gradients of sum(dout * out) with respect to q, k and v, for training
+ * (LongNet package README, "Key Advantages": training runs and the
+ * distributed trainer; LONGNET blog, "Token expansion reaches 1 billion+").
+ * With the merge above, a row's output is one softmax over the multiset of
+ * (pattern, key) pairs its covering patterns give it, so with the merged
+ * lse and D = dout . out of each row:
+ *     P = exp(scale q.k - lse),  dS = P (dout . v - D),
+ *     dq = scale sum dS k,  dk = scale sum dS q,  dv = sum P dout,
+ * summed over every (pattern, segment) that gathers both rows. Rows no
+ * pattern gathers get zero gradients.
+ *
+ * Inputs: q, k, v as given to dilated_attn_fwd; out and lse as it returned
+ * them (same patterns, causal flag and scale); dout [B, N, H, Dh] in the
+ * element type of q. Outputs: dq, dk, dv [B, N, H, Dh] in that element type,
+ * every element written. Same alignment rules as the forward pass (the
+ * tensors 16-byte, lse 4-byte, workspace 256-byte aligned). dq, dk, dv and
+ * the workspace must not overlap each other or any input (DA_ERR_ALIAS);
+ * inputs may overlap each other. The workspace is required (it holds D) and
+ * its contents on entry are ignored. */
+
+/* Bytes of device workspace dilated_attn_bwd needs: one float per row for D
+ * and, for two or more patterns, the per-pattern fp32 partial dq, dk, dv rows
+ * of rows several patterns gather. Writes *bytes and returns DA_OK, or an
+ * error code for invalid arguments. */
+int dilated_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
+                                     const da_pattern* patterns, int32_t n_patterns,
+                                     int32_t dtype, size_t* bytes);
+
+/* The whole backward pass. Returns DA_OK or a DA_ERR_* code. */
+int dilated_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                     int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns,
+                     int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stages of dilated_attn_bwd, for timing each kernel. Launched in this
+ * order on one stream, all four are exactly dilated_attn_bwd:
+ *  DA_BWD_PREP:  D = dout . out of every row into the workspace;
+ *  DA_BWD_KV:    dk and dv of every row one pattern gathers, workspace
+ *                partials of rows several patterns gather (needs D);
+ *  DA_BWD_Q:     the same for dq (needs D);
+ *  DA_BWD_MERGE: sums the partials of rows several patterns gather and
+ *                writes zeros to rows no pattern gathers.
+ * stages is a non-empty OR of these flags (else DA_ERR_ARG); the other
+ * arguments and checks are those of dilated_attn_bwd. */
+enum { DA_BWD_PREP = 1, DA_BWD_KV = 2, DA_BWD_Q = 4, DA_BWD_MERGE = 8, DA_BWD_ALL = 15 };
+int dilated_attn_bwd_stages(int32_t stages, const void* q, const void* k, const void* v,
+                            const void* out, const float* lse, const void* dout, void* dq,
+                            void* dk, void* dv, int64_t B, int64_t N, int32_t H, int32_t Dh,
+                            const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                            int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Test hook: the gather map the kernels use, written by a device kernel
  * through the same index function as the attention kernel.

@@ -1,19 +1,24 @@
-"""Dilated attention (LongNet) forward pass for AMD MI355X (gfx950).
+"""Dilated attention (LongNet) forward and backward passes for AMD MI355X
+(gfx950).
 
 Python face of the C-ABI library: ``dilated_attn`` takes projected q, k, v
 of shape [B, N, H, 64] (bf16 or fp32, on the GPU) and a list of
 (segment length w, dilation r) patterns, and returns (out [B, N, H, 64],
-lse [B, H, N] float32). All computation happens in the HIP kernels; torch
+lse [B, H, N] float32); ``dilated_attn_bwd`` takes those plus dout and
+returns (dq, dk, dv). All computation happens in the HIP kernels; torch
 only allocates memory and supplies the current stream.
 """
 from . import _native
-from ._native import (DA_BF16, DA_F32, DA_HEAD_DIM, DA_MAX_PATTERNS, DilatedAttnError,
+from ._native import (DA_BF16, DA_BWD_ALL, DA_BWD_KV, DA_BWD_MERGE, DA_BWD_PREP, DA_BWD_Q, DA_F32,
+                      DA_HEAD_DIM, DA_MAX_PATTERNS, DilatedAttnError, bwd_workspace_bytes,
                       load_library, strerror, version, workspace_bytes)
 
 __all__ = [
     "dilated_attn", "dilated_attn_attention_stage", "dilated_attn_merge_stage", "gather_map",
     "coverage_map", "workspace_bytes", "strerror", "version", "load_library", "DilatedAttnError",
-    "DA_F32", "DA_BF16", "DA_HEAD_DIM", "DA_MAX_PATTERNS", "Problem",
+    "DA_F32", "DA_BF16", "DA_HEAD_DIM", "DA_MAX_PATTERNS", "Problem", "dilated_attn_bwd",
+    "BwdProblem", "bwd_workspace_bytes", "DA_BWD_PREP", "DA_BWD_KV", "DA_BWD_Q", "DA_BWD_MERGE",
+    "DA_BWD_ALL",
 ]
 
 
@@ -88,6 +93,70 @@ class Problem:
 
     def merge_stage(self, stream=None):
         self._call("dilated_attn_fwd_merge", stream)
+
+
+class BwdProblem:
+    """Validated tensors and buffers of one backward call: q, k, v, out, lse
+    as in the forward call, dout like q; dq, dk, dv and the workspace are
+    allocated unless given."""
+
+    def __init__(self, q, k, v, out, lse, dout, patterns, causal=True, scale=None, dq=None,
+                 dk=None, dv=None, workspace=None):
+        import torch
+
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be on the GPU (got {t.device}); no CPU path exists")
+            if t.dim() != 4 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [B, N, H, Dh] tensor")
+            if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+                raise ValueError(f"{name} must match q in shape, dtype and device")
+        self.q, self.k, self.v, self.out, self.dout = q, k, v, out, dout
+        self.B, self.N, self.H, self.Dh = (int(x) for x in q.shape)
+        if (not isinstance(lse, torch.Tensor) or lse.shape != (self.B, self.H, self.N)
+                or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device):
+            raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+        self.lse = lse
+        self.patterns = [(int(w), int(r)) for (w, r) in patterns]
+        self.causal = bool(causal)
+        self.scale = float(scale) if scale else 0.0
+        self.dtype = _dtype_code(q)
+        self._pats = _native.pattern_array(self.patterns)
+        self.dq = dq if dq is not None else torch.empty_like(q)
+        self.dk = dk if dk is not None else torch.empty_like(q)
+        self.dv = dv if dv is not None else torch.empty_like(q)
+        for name, t in (("dq", self.dq), ("dk", self.dk), ("dv", self.dv)):
+            if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous tensor like q")
+        ws = bwd_workspace_bytes(self.B, self.N, self.H, self.Dh, self.patterns, self.dtype)
+        if workspace is None:
+            workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        self.workspace = workspace
+        self.ws_bytes = workspace.numel() * workspace.element_size()
+
+    def run(self, stages=DA_BWD_ALL, stream=None):
+        import torch
+
+        lib = load_library()
+        if stream is None:
+            stream = torch.cuda.current_stream(self.q.device)
+        code = lib.dilated_attn_bwd_stages(
+            int(stages), self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+            self.out.data_ptr(), self.lse.data_ptr(), self.dout.data_ptr(), self.dq.data_ptr(),
+            self.dk.data_ptr(), self.dv.data_ptr(), self.B, self.N, self.H, self.Dh, self._pats,
+            len(self.patterns), 1 if self.causal else 0, self.dtype, self.scale,
+            self.workspace.data_ptr(), self.ws_bytes, stream.cuda_stream)
+        _native.check(code, "dilated_attn_bwd_stages")
+        return self.dq, self.dk, self.dv
+
+
+def dilated_attn_bwd(q, k, v, out, lse, dout, patterns, causal=True, scale=None, dq=None, dk=None,
+                     dv=None, workspace=None):
+    """Dilated-attention backward. Returns (dq, dk, dv); see include/dilated_attn.h."""
+    return BwdProblem(q, k, v, out, lse, dout, patterns, causal, scale, dq, dk, dv,
+                      workspace).run()
 
 
 def dilated_attn(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, workspace=None):

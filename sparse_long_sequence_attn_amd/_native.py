@@ -32,12 +32,19 @@ class DaPattern(ctypes.Structure):
 
 _FWD_ARGS = [_P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I32, ctypes.c_float,
              _P, _SZ, _P]
+_BWD_ARGS = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P, _I32, _I32, _I32,
+             ctypes.c_float, _P, _SZ, _P]
+DA_BWD_PREP, DA_BWD_KV, DA_BWD_Q, DA_BWD_MERGE, DA_BWD_ALL = 1, 2, 4, 8, 15
 SIGNATURES = {
     "dilated_attn_workspace_bytes": ([_I64, _I64, _I32, _I32, _P, _I32, _I32,
                                       ctypes.POINTER(_SZ)], ctypes.c_int),
     "dilated_attn_fwd": (_FWD_ARGS, ctypes.c_int),
     "dilated_attn_fwd_attention": (_FWD_ARGS, ctypes.c_int),
     "dilated_attn_fwd_merge": (_FWD_ARGS, ctypes.c_int),
+    "dilated_attn_bwd_workspace_bytes": ([_I64, _I64, _I32, _I32, _P, _I32, _I32,
+                                          ctypes.POINTER(_SZ)], ctypes.c_int),
+    "dilated_attn_bwd": (_BWD_ARGS, ctypes.c_int),
+    "dilated_attn_bwd_stages": ([_I32] + _BWD_ARGS, ctypes.c_int),
     "dilated_attn_gather_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, _P], ctypes.c_int),
     "dilated_attn_coverage_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, _P], ctypes.c_int),
     "dilated_attn_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -98,4 +105,13 @@ def workspace_bytes(B, N, H, Dh, patterns, dtype):
     code = load_library().dilated_attn_workspace_bytes(B, N, H, Dh, pattern_array(patterns),
                                                        len(patterns), dtype, ctypes.byref(out))
     check(code, "dilated_attn_workspace_bytes")
+    return out.value
+
+
+def bwd_workspace_bytes(B, N, H, Dh, patterns, dtype):
+    out = _SZ(0)
+    code = load_library().dilated_attn_bwd_workspace_bytes(B, N, H, Dh, pattern_array(patterns),
+                                                           len(patterns), dtype,
+                                                           ctypes.byref(out))
+    check(code, "dilated_attn_bwd_workspace_bytes")
     return out.value

@@ -20,6 +20,14 @@ using da::PatDev;
 constexpr int64_t kMaxGrid = 0x7fffffff;
 constexpr float kLog2e = 1.44269504088896340736f;
 
+// Order of the tiles of all patterns in one launch (see AttnArgs).
+struct TileOrder {
+  int32_t ntile[kMaxPat];  // tiles per unit, caller's pattern order
+  int order[kMaxPat];      // pattern indices sorted by ntile, descending
+  int64_t unit_start[kMaxPat + 1];
+  int64_t grid = 0;  // kXcds * (longest per-XCD tile list)
+};
+
 struct Plan {
   bool empty = false;
   bool bf16 = false;
@@ -29,17 +37,56 @@ struct Plan {
   int64_t B = 0, N = 0;
   int32_t H = 0;
   float sl2 = 0.f;
+  float scale = 0.f;
   PatDev pat[kMaxPat];     // caller's order
-  int order[kMaxPat];      // pattern indices sorted by ntile, descending
-  int64_t unit_start[kMaxPat + 1];
-  int64_t total_tiles = 0;
-  int64_t grid = 0;  // kXcds * (longest per-XCD tile list)
+  TileOrder fwd;           // forward attention tiles
+  TileOrder bwd;           // backward tiles (32 * nw rows)
   size_t ws_bytes = 0;
   size_t tensor_bytes = 0;
   size_t lse_bytes = 0;
+  // backward workspace: D at float offset 0, then per pattern (two or more
+  // patterns) the dq, dk, dv partial blocks at bwd_po_off[i]
+  int64_t bwd_po_off[kMaxPat];
+  size_t bwd_ws_bytes = 0;
 };
 
 int64_t align64(int64_t x) { return (x + 63) & ~int64_t(63); }
+
+// Tiles of bm rows per unit, patterns sorted by tile count (descending),
+// units dealt to the XCDs round-robin in that order; grid = kXcds times the
+// longest per-XCD tile list.
+int tile_order(const Plan* pl, int bm, TileOrder* to) {
+  const int np = pl->np;
+  for (int i = 0; i < np; ++i) to->ntile[i] = (pl->pat[i].lmax + bm - 1) / bm;
+  for (int i = 0; i < np; ++i) to->order[i] = i;
+  std::stable_sort(to->order, to->order + np,
+                   [&](int x, int y) { return to->ntile[x] > to->ntile[y]; });
+  to->unit_start[0] = 0;
+  for (int j = 0; j < np; ++j)
+    to->unit_start[j + 1] = to->unit_start[j] + pl->pat[to->order[j]].units;
+  int64_t per_xcd[da::kXcds] = {0};
+  for (int j = 0; j < np; ++j) {
+    const int64_t u0 = to->unit_start[j], u1 = to->unit_start[j + 1];
+    for (int x = 0; x < da::kXcds; ++x) {
+      const int64_t first = u0 + (((x - u0) % da::kXcds) + da::kXcds) % da::kXcds;
+      const int64_t cnt = first < u1 ? (u1 - first + da::kXcds - 1) / da::kXcds : 0;
+      per_xcd[x] += cnt * to->ntile[to->order[j]];
+    }
+  }
+  int64_t longest = 0;
+  for (int x = 0; x < da::kXcds; ++x) longest = std::max(longest, per_xcd[x]);
+  to->grid = longest * da::kXcds;
+  return to->grid > kMaxGrid ? DA_ERR_SHAPE : DA_OK;
+}
+
+// Patterns in a launch's sorted order, with that launch's tile counts.
+void sorted_patterns(const Plan& pl, const TileOrder& to, PatDev* dst, int64_t* unit_start) {
+  for (int j = 0; j < pl.np; ++j) {
+    dst[j] = pl.pat[to.order[j]];
+    dst[j].ntile = to.ntile[to.order[j]];
+  }
+  for (int j = 0; j <= pl.np; ++j) unit_start[j] = to.unit_start[j];
+}
 
 // Shapes, patterns, dtype and scalars; computes everything that does not
 // depend on pointers.
@@ -74,6 +121,7 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
   pl->H = H;
   const double sc = scale > 0.f ? (double)scale : 1.0 / sqrt((double)Dh);
   pl->sl2 = (float)(sc * (double)kLog2e);
+  pl->scale = (float)sc;
   pl->tensor_bytes = (size_t)(B * N * H * Dh) * (pl->bf16 ? 2 : 4);
   pl->lse_bytes = (size_t)(B * N * H) * 4;
   pl->empty = B == 0 || N == 0 || H == 0;
@@ -94,34 +142,10 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
   }
   // one 32-row wave per workgroup when every segment is that short
   pl->nw = lmax_all > 32 ? 4 : 1;
-  const int bm = da::attn_tile_rows(pl->bf16, pl->nw);
-  for (int i = 0; i < n_patterns; ++i) pl->pat[i].ntile = (pl->pat[i].lmax + bm - 1) / bm;
-
-  for (int i = 0; i < n_patterns; ++i) pl->order[i] = i;
-  std::stable_sort(pl->order, pl->order + n_patterns,
-                   [&](int x, int y) { return pl->pat[x].ntile > pl->pat[y].ntile; });
-  pl->unit_start[0] = 0;
-  for (int j = 0; j < n_patterns; ++j)
-    pl->unit_start[j + 1] = pl->unit_start[j] + pl->pat[pl->order[j]].units;
-  // per-XCD tile lists (units dealt round-robin in sorted order)
-  int64_t per_xcd[da::kXcds] = {0};
-  for (int j = 0; j < n_patterns; ++j) {
-    const PatDev& p = pl->pat[pl->order[j]];
-    for (int x = 0; x < da::kXcds; ++x) {
-      const int64_t u0 = pl->unit_start[j], u1 = pl->unit_start[j + 1];
-      const int64_t first = u0 + (((x - u0) % da::kXcds) + da::kXcds) % da::kXcds;
-      const int64_t cnt = first < u1 ? (u1 - first + da::kXcds - 1) / da::kXcds : 0;
-      per_xcd[x] += cnt * p.ntile;
-    }
-  }
-  pl->total_tiles = 0;
-  int64_t longest = 0;
-  for (int x = 0; x < da::kXcds; ++x) {
-    pl->total_tiles += per_xcd[x];
-    longest = std::max(longest, per_xcd[x]);
-  }
-  pl->grid = longest * da::kXcds;
-  if (pl->grid > kMaxGrid) return DA_ERR_SHAPE;
+  int rc = tile_order(pl, da::attn_tile_rows(pl->bf16, pl->nw), &pl->fwd);
+  if (rc != DA_OK) return rc;
+  rc = tile_order(pl, 32 * pl->nw, &pl->bwd);
+  if (rc != DA_OK) return rc;
 
   // partial outputs and log2-sum-exp per pattern, 256-byte aligned regions
   int64_t cur = 0;
@@ -136,6 +160,17 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
     }
   }
   pl->ws_bytes = (size_t)cur * 4;
+
+  // backward: D per row, then dq, dk, dv partial blocks per pattern
+  cur = align64(B * H * N);
+  for (int i = 0; i < n_patterns; ++i) {
+    pl->bwd_po_off[i] = -1;
+    if (n_patterns > 1) {
+      pl->bwd_po_off[i] = cur;
+      cur += align64(3 * B * H * pl->pat[i].nseg * pl->pat[i].lmax * kDh);
+    }
+  }
+  pl->bwd_ws_bytes = (size_t)cur * 4;
   return DA_OK;
 }
 
@@ -178,10 +213,9 @@ int run_attention(const Plan& pl, const void* q, const void* k, const void* v, v
   a.H = pl.H;
   a.np = pl.np;
   a.sl2 = pl.sl2;
-  for (int j = 0; j < pl.np; ++j) a.pat[j] = pl.pat[pl.order[j]];
-  for (int j = 0; j <= pl.np; ++j) a.unit_start[j] = pl.unit_start[j];
+  sorted_patterns(pl, pl.fwd, a.pat, a.unit_start);
   const hipError_t e =
-      da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.grid, st);
+      da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.fwd.grid, st);
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
@@ -219,6 +253,95 @@ int fwd_common(int stages, const void* q, const void* k, const void* v, void* ou
   }
   if (stages & kMerge) rc = run_merge(pl, out, lse, workspace, st);
   return rc;
+}
+
+// ---------------------------------------------------------------- backward
+
+int check_bwd_buffers(const Plan& pl, const void* q, const void* k, const void* v,
+                      const void* out, const float* lse, const void* dout, const void* dq,
+                      const void* dk, const void* dv, const void* ws, size_t ws_bytes) {
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return DA_ERR_NULL;
+  if (!ws || ws_bytes < pl.bwd_ws_bytes) return DA_ERR_WORKSPACE;
+  auto mis = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
+  const void* t16[8] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* t : t16)
+    if (mis(t, 16)) return DA_ERR_ALIGN;
+  if (mis(lse, 4) || mis(ws, 256)) return DA_ERR_ALIGN;
+  const size_t tb = pl.tensor_bytes, lb = pl.lse_bytes, wb = pl.bwd_ws_bytes;
+  const void* outs[4] = {dq, dk, dv, ws};
+  const size_t osz[4] = {tb, tb, tb, wb};
+  const void* ins[6] = {q, k, v, out, dout, lse};
+  const size_t isz[6] = {tb, tb, tb, tb, tb, lb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return DA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return DA_ERR_ALIAS;
+  }
+  return DA_OK;
+}
+
+int bwd_common(int stages, const void* q, const void* k, const void* v, const void* out,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
+               int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
+               int32_t causal, int32_t dtype, float scale, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (stages < 1 || stages > DA_BWD_ALL) return DA_ERR_ARG;
+  Plan pl;
+  int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
+  if (rc != DA_OK || pl.empty) return rc;
+  rc = check_bwd_buffers(pl, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes);
+  if (rc != DA_OK) return rc;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  float* ws = reinterpret_cast<float*>(workspace);
+
+  da::BwdRowArgs ra;
+  memset(&ra, 0, sizeof ra);
+  ra.out = out;
+  ra.dout = dout;
+  ra.dvec = ws;
+  ra.dq = dq;
+  ra.dk = dk;
+  ra.dv = dv;
+  ra.ws = ws;
+  ra.B = pl.B;
+  ra.N = pl.N;
+  ra.H = pl.H;
+  ra.np = pl.np;
+  for (int i = 0; i < pl.np; ++i) {
+    ra.pat[i] = pl.pat[i];
+    ra.pat[i].po_off = pl.bwd_po_off[i];
+  }
+
+  da::BwdArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dvec = ws;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = ws;
+  a.B = pl.B;
+  a.N = pl.N;
+  a.H = pl.H;
+  a.np = pl.np;
+  a.sl2 = pl.sl2;
+  a.scale = pl.scale;
+  sorted_patterns(pl, pl.bwd, a.pat, a.unit_start);
+  for (int j = 0; j < pl.np; ++j) a.pat[j].po_off = pl.bwd_po_off[pl.bwd.order[j]];
+
+  hipError_t e = hipSuccess;
+  if (stages & DA_BWD_PREP) e = da::launch_bwd_prep(ra, pl.bf16, st);
+  if (e == hipSuccess && (stages & DA_BWD_KV))
+    e = da::launch_bwd_kv(a, pl.bf16, pl.nw, pl.causal, pl.bwd.grid, st);
+  if (e == hipSuccess && (stages & DA_BWD_Q))
+    e = da::launch_bwd_q(a, pl.bf16, pl.nw, pl.causal, pl.bwd.grid, st);
+  if (e == hipSuccess && (stages & DA_BWD_MERGE)) e = da::launch_bwd_merge(ra, pl.bf16, st);
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
 // Geometry of one pattern for the map hooks.
@@ -278,6 +401,36 @@ int dilated_attn_fwd_merge(const void* q, const void* k, const void* v, void* ou
                            void* stream) {
   return fwd_common(kMerge, q, k, v, out, lse, B, N, H, Dh, patterns, n_patterns, causal, dtype,
                     scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
+                                     const da_pattern* patterns, int32_t n_patterns,
+                                     int32_t dtype, size_t* bytes) {
+  if (!bytes) return DA_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(B, N, H, Dh, patterns, n_patterns, 1, dtype, 0.f, &pl);
+  if (rc != DA_OK) return rc;
+  *bytes = pl.empty ? 0 : pl.bwd_ws_bytes;
+  return DA_OK;
+}
+
+int dilated_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                     int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns,
+                     int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_common(DA_BWD_ALL, q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Dh, patterns,
+                    n_patterns, causal, dtype, scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_bwd_stages(int32_t stages, const void* q, const void* k, const void* v,
+                            const void* out, const float* lse, const void* dout, void* dq,
+                            void* dk, void* dv, int64_t B, int64_t N, int32_t H, int32_t Dh,
+                            const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                            int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return bwd_common(stages, q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Dh, patterns,
+                    n_patterns, causal, dtype, scale, workspace, workspace_bytes, stream);
 }
 
 int dilated_attn_gather_map(int64_t N, int32_t H, da_pattern pattern, int32_t h, int64_t* dev_out,

@@ -1,0 +1,736 @@
+// Backward pass of dilated attention for gfx950 (MI355X).
+//
+// LongNet is trained (LongNet package README, "Key Advantages": training
+// runs and the distributed trainer; LONGNET blog, "Token expansion reaches
+// 1 billion+": training split along the sequence), so the path needs the
+// gradients of the forward pass. The merged output of a row is one softmax
+// over the multiset of (pattern, key) pairs that its covering patterns give
+// it (the log-sum-exp merge reading), so with the merged lse and
+// D = dout . out of each row, every pattern's segments contribute
+// independently:
+//   P = exp(scale q.k - lse),  dP = dout . v,  dS = P (dP - D),
+//   dq += scale dS k,  dk += scale dS^T q,  dv += P^T dout,
+// summed over the patterns that gather a row.
+//
+// Kernels:
+//  * bwd_prep_kernel: D for every row.
+//  * bwd_kv_kernel: one workgroup per tile of 32 * NW gathered keys of one
+//    (pattern, batch, head, segment) unit. Each wave keeps its 32 keys' K and
+//    V fragments and the dK^T, dV^T accumulators in registers and streams
+//    the unit's query rows (Q, dout, lse, D) through LDS, double buffered.
+//    S = Q K^T puts one key in each lane and 16 of its queries in registers,
+//    which is the B-operand layout of dV^T += dout^T P and dK^T += Q^T dS;
+//    their A operands (8 queries of one dimension per lane) come from the
+//    LDS transpose read.
+//  * bwd_q_kernel: one workgroup per tile of 32 * NW gathered queries, in the
+//    forward kernel's layout (S^T = K Q^T: one query per lane), K and V
+//    streamed through LDS; dQ^T += K^T dS^T takes K^T from the transpose read.
+//  * bwd_merge_kernel: rows several patterns gather add up their fp32
+//    partials; rows no pattern gathers get zero gradients.
+// bf16 inputs use v_mfma_f32_32x32x16_bf16 with P and dS rounded to bf16 as
+// MFMA operands; fp32 inputs use v_mfma_f32_32x32x2_f32 throughout.
+//
+// Rows past a segment's last gathered row load as zeros (buffer range
+// checks) and get lse = +inf and D = 0, so their P and dS are exactly 0; keys
+// past it have K = V = 0 and add nothing to dQ, and their own dK, dV are
+// never stored.
+#include <type_traits>
+
+#include "da_bwd.hpp"
+#include "da_device.hpp"
+#include "kernels.hpp"
+
+namespace da {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// LDS row stride in elements: bf16 rows of 72 elements (144 bytes), so the
+// 16 lanes the LDS serves together when reading 16-byte chunks of 16
+// consecutive rows hit distinct bank groups, and the transpose read applies;
+// fp32 rows of 65 floats.
+template <bool BF>
+constexpr int lds_stride() {
+  return BF ? kDh + 8 : kDh + 1;
+}
+
+// Byte offset of a lane's LDS transpose read inside a 16 x 32 block of a
+// bf16 tile with row stride ST: in 16-lane group g (n = 16 (g & 1) + i,
+// hh = g >> 1) lane m points at row 8 h' + 4 hh + m / 4 (h' = 0 for the first
+// read, 1 for the second, 8 rows further), columns 16 (g & 1) + 4 (m & 3) ..
+// +3; the read then hands lane i the four rows of column i. Two reads give a
+// lane rows {0..3, 8..11} + 4 hh of its column: the k order
+// 16c + 8(e / 4) + 4hh + e % 4 that matches the MFMA output layout.
+template <int ST>
+__device__ inline uint32_t tr_lane_offset(int lane) {
+  const int m16 = lane & 15, g16 = lane >> 4;
+  return (uint32_t)((4 * (g16 >> 1) + (m16 >> 2)) * ST + 16 * (g16 & 1) + 4 * (m16 & 3)) * 2;
+}
+
+__device__ inline bf16x8 tr_fragment(lds_cptr base, uint32_t off, int ST) {
+  const u32x2 lo = dev_read_tr16(base, off);
+  const u32x2 hi = dev_read_tr16(base, off + 8 * ST * 2);
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+__device__ inline bf16x8 to_bf16x8(const float* x) {
+  u32x4 u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) u[i] = dev_pack_bf16(x[2 * i], x[2 * i + 1]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Gathered-row geometry of one tile's unit.
+struct UnitGeom {
+  int32_t r, off, L;
+  int64_t wp, seg0, headbase, rs, bh;
+  uint32_t mbytes, range;
+};
+
+template <class T>
+__device__ inline UnitGeom unit_geom(const BwdArgs& a, const UnitTile& tl) {
+  UnitGeom g;
+  const PatDev& P = a.pat[tl.p];
+  g.r = P.r;
+  g.wp = P.wp;
+  g.off = head_offset(tl.h, g.r);
+  g.L = rows_gathered(g.wp, g.off, g.r);
+  g.rs = (int64_t)a.H * kDh;
+  g.seg0 = tl.seg * g.wp;
+  g.headbase = tl.b * a.N * g.rs + (int64_t)tl.h * kDh;
+  g.bh = tl.b * a.H + tl.h;
+  // gathered row m of the unit starts m * mbytes bytes after row 0; the host
+  // keeps these offsets (plus one tile of overrun) below 2^31
+  g.mbytes = (uint32_t)((int64_t)g.r * g.rs * (int64_t)sizeof(T));
+  g.range = (uint32_t)(g.L - 1) * g.mbytes + (uint32_t)(kDh * sizeof(T));
+  return g;
+}
+
+// Register fragments of gathered row m of one tensor as an MFMA operand
+// with the row in the lane: bf16 - dims 16 ks + 8 hh .. +7 for ks = 0..3;
+// fp32 - dim 2 ks + hh for ks = 0..31.
+template <bool BF>
+struct RowFrag {
+  typename std::conditional<BF, bf16x8, float>::type x[BF ? 4 : 32];
+  __device__ inline void load(__amdgpu_buffer_rsrc_t rsrc, uint32_t row_off, int hh) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        x[ks] = __builtin_bit_cast(bf16x8, dev_load16(rsrc, row_off + (16 * ks + 8 * hh) * 2));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const f32x4 v = __builtin_bit_cast(f32x4, dev_load16(rsrc, row_off + 16 * c));
+        x[2 * c] = hh ? v[1] : v[0];
+        x[2 * c + 1] = hh ? v[3] : v[2];
+      }
+    }
+  }
+};
+
+// Stages R gathered rows of two tensors (16-byte chunks: global ->
+// registers -> LDS) for a workgroup of NT threads.
+template <bool BF, int R, int NT>
+struct PairStager {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  static constexpr int ST = lds_stride<BF>();
+  static constexpr int kChunksPerRow = kDh * (int)sizeof(T) / 16;
+  static constexpr int CK = R * kChunksPerRow / NT;
+  static_assert(CK >= 1 && R * kChunksPerRow % NT == 0, "tile too small for the workgroup");
+  u32x4 ra[CK], rb[CK];
+  uint32_t off[CK];
+
+  __device__ inline void init(int tid, uint32_t mbytes) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int c = tid + i * NT;
+      off[i] = (uint32_t)(c / kChunksPerRow) * mbytes + (uint32_t)(c % kChunksPerRow) * 16;
+    }
+  }
+  __device__ inline void load(__amdgpu_buffer_rsrc_t sa, __amdgpu_buffer_rsrc_t sb, uint32_t base) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      ra[i] = dev_load16(sa, base + off[i]);
+      rb[i] = dev_load16(sb, base + off[i]);
+    }
+  }
+  __device__ inline void store(int tid, T* A, T* B) const {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
+      if constexpr (BF) {
+        *reinterpret_cast<u32x4*>(A + row * ST + ch * 8) = ra[i];
+        *reinterpret_cast<u32x4*>(B + row * ST + ch * 8) = rb[i];
+      } else {
+        float* da = reinterpret_cast<float*>(A) + row * ST + 4 * ch;
+        float* db = reinterpret_cast<float*>(B) + row * ST + 4 * ch;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          da[e] = __uint_as_float(ra[i][e]);
+          db[e] = __uint_as_float(rb[i][e]);
+        }
+      }
+    }
+  }
+};
+
+// Writes one lane's half of a gradient row held in MFMA output layout (two
+// 32-dim blocks; register 4g + e of block db is dim db*32 + 8g + 4hh + e),
+// multiplied by mul, either into the final tensor or into an fp32 partial.
+template <bool BF>
+__device__ inline void put_row(void* dst_tensor, int64_t elem_off, const f32x16 (&acc)[2],
+                               float mul, int hh) {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  T* dst = reinterpret_cast<T*>(dst_tensor) + elem_off + 4 * hh;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + 8 * g;
+      if constexpr (BF) {
+        *reinterpret_cast<u32x2*>(dst + d) =
+            u32x2{dev_pack_bf16(acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                  dev_pack_bf16(acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      } else {
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * mul;
+        *reinterpret_cast<f32x4*>(dst + d) = x;
+      }
+    }
+}
+
+__device__ inline void put_partial(float* dst, const f32x16 (&acc)[2], float mul, int hh) {
+  dst += 4 * hh;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * mul;
+      *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * g) = x;
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int NW, bool CAUSAL, bool BF>
+__global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  constexpr int BQ = NW == 4 ? 64 : 32;  // query rows per LDS tile
+  constexpr int QBT = BQ / 32;
+  constexpr int NT = 64 * NW;
+  constexpr int ST = lds_stride<BF>();
+  constexpr int kTileElems = BQ * ST;
+  constexpr int kTileBytes = kTileElems * (int)sizeof(T);
+  constexpr int kBufBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dout, lse2, D
+  static_assert(kTileBytes % 16 == 0, "LDS alignment");
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+
+  UnitTile tl;
+  if (!decode_unit_tile<false>(a, blockIdx.x, &tl)) return;
+  const UnitGeom g = unit_geom<T>(a, tl);
+  const int32_t k0 = tl.tile * 32 * NW;
+  if (k0 >= g.L) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t rowbase = g.headbase + (g.seg0 + g.off) * g.rs;
+  const auto rq = dev_rsrc(reinterpret_cast<const T*>(a.q) + rowbase, g.range);
+  const auto rk = dev_rsrc(reinterpret_cast<const T*>(a.k) + rowbase, g.range);
+  const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, g.range);
+  const auto rdo = dev_rsrc(reinterpret_cast<const T*>(a.dout) + rowbase, g.range);
+  const float* lse_row = a.lse + g.bh * a.N;
+  const float* d_row = a.dvec + g.bh * a.N;
+
+  const int32_t kw0 = k0 + 32 * wv;  // this wave's first key
+  const int32_t mk = kw0 + n;        // this lane's key
+  RowFrag<BF> kf, vf;                // B operands of S = Q K^T and dP = dout V^T
+  kf.load(rk, (uint32_t)mk * g.mbytes, hh);
+  vf.load(rv, (uint32_t)mk * g.mbytes, hh);
+
+  f32x16 dK[2], dV[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dK[db][v] = dV[db][v] = 0.f;
+
+  // query tiles: from this workgroup's first key (causal) or row 0
+  const int32_t qstart = CAUSAL ? k0 : 0;  // a multiple of BQ
+  const int32_t nqt = (g.L - qstart + BQ - 1) / BQ;
+
+  PairStager<BF, BQ, NT> stg;
+  stg.init(tid, g.mbytes);
+  float lreg = 0.f, dreg = 0.f;  // lse2 and D of query row tid of the next tile
+  auto load_tile = [&](int t) {
+    const int32_t m0 = qstart + t * BQ;
+    stg.load(rq, rdo, (uint32_t)m0 * g.mbytes);
+    if (tid < BQ) {
+      const int32_t m = m0 + tid;
+      lreg = INFINITY;
+      dreg = 0.f;
+      if (m < g.L) {
+        const int64_t pos = g.seg0 + g.off + (int64_t)m * g.r;
+        lreg = lse_row[pos] * kLog2e;
+        dreg = d_row[pos];
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* base = smem + buf * kBufBytes;
+    stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
+    if (tid < BQ) {
+      float* ls = reinterpret_cast<float*>(base + 2 * kTileBytes);
+      ls[tid] = lreg;
+      ls[BQ + tid] = dreg;
+    }
+  };
+
+  const float sl2 = a.sl2;
+  const uint32_t trl = tr_lane_offset<ST>(lane);
+
+  auto compute = [&](int buf, int t) {
+    const char* base = smem + buf * kBufBytes;
+    const T* Qs = reinterpret_cast<const T*>(base);
+    const T* Ds = reinterpret_cast<const T*>(base + kTileBytes);
+    const float* ls = reinterpret_cast<const float*>(base + 2 * kTileBytes);
+    const float* dd = ls + BQ;
+#pragma unroll
+    for (int qb = 0; qb < QBT; ++qb) {
+      const int32_t qs = qstart + t * BQ + 32 * qb;  // first query of the block
+      if (qs >= g.L) break;
+      if (CAUSAL && qs < kw0) continue;  // 32-aligned: every query precedes every key
+      const int row = qb * 32 + n;
+      f32x16 S, dP;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[v] = dP[v] = 0.f;
+      if constexpr (BF) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + row * ST + 16 * ks + 8 * hh);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + row * ST + 16 * ks + 8 * hh);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf.x[ks], S, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf.x[ks], dP, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          const float qa = reinterpret_cast<const float*>(Qs)[row * ST + 2 * ks + hh];
+          const float da = reinterpret_cast<const float*>(Ds)[row * ST + 2 * ks + hh];
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(qa, kf.x[ks], S, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_f32_32x32x2f32(da, vf.x[ks], dP, 0, 0, 0);
+        }
+      }
+      // register v: query qb*32 + 8(v/4) + 4hh + v%4 of the tile, key n
+      float pv[16], sv[16];
+      const bool diag = CAUSAL && qs == kw0;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int qi = qb * 32 + 8 * gq + 4 * hh;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qi);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + qi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = 4 * gq + j;
+          float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l4[j]));
+          if (diag && 8 * gq + 4 * hh + j < n) p = 0.f;
+          pv[v] = p;
+          sv[v] = p * (dP[v] - d4[j]);
+        }
+      }
+      if constexpr (BF) {
+        const lds_cptr qbase = (lds_cptr)smem + buf * kBufBytes;
+        const lds_cptr dbase = qbase + kTileBytes;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 pb = to_bf16x8(pv + 8 * c);
+          const bf16x8 sb = to_bf16x8(sv + 8 * c);
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            const uint32_t o = trl + (uint32_t)((qb * 32 + 16 * c) * ST + db * 32) * 2;
+            dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(dbase, o, ST), pb, dV[db],
+                                                             0, 0, 0);
+            dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qbase, o, ST), sb, dK[db],
+                                                             0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int qi = qb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            const float dov = reinterpret_cast<const float*>(Ds)[qi * ST + db * 32 + n];
+            const float qv = reinterpret_cast<const float*>(Qs)[qi * ST + db * 32 + n];
+            dV[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(dov, pv[v], dV[db], 0, 0, 0);
+            dK[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(qv, sv[v], dK[db], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < nqt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nqt) load_tile(t + 1);
+    compute(buf, t);
+    if (t + 1 < nqt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (mk >= g.L) return;
+  const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
+  if (coverage(a, (uint32_t)pos, tl.h) == 1) {
+    const int64_t e = g.headbase + pos * g.rs;
+    put_row<BF>(a.dk, e, dK, a.scale, hh);
+    put_row<BF>(a.dv, e, dV, 1.f, hh);
+  } else {
+    const PatDev& P = a.pat[tl.p];
+    const int64_t slots = P.units * P.lmax;
+    const int64_t prow = (g.bh * P.nseg + tl.seg) * P.lmax + mk;
+    put_partial(a.ws + P.po_off + (slots + prow) * kDh, dK, a.scale, hh);
+    put_partial(a.ws + P.po_off + (2 * slots + prow) * kDh, dV, 1.f, hh);
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int NW, bool CAUSAL, bool BF>
+__global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  constexpr int BK = NW == 4 ? 64 : 32;  // key rows per LDS tile
+  constexpr int KBT = BK / 32;
+  constexpr int NT = 64 * NW;
+  constexpr int ST = lds_stride<BF>();
+  constexpr int kTileBytes = BK * ST * (int)sizeof(T);
+  constexpr int kBufBytes = 2 * kTileBytes;  // K, V
+  static_assert(kTileBytes % 16 == 0, "LDS alignment");
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+
+  UnitTile tl;
+  if (!decode_unit_tile<CAUSAL>(a, blockIdx.x, &tl)) return;
+  const UnitGeom g = unit_geom<T>(a, tl);
+  const int32_t q0 = tl.tile * 32 * NW;
+  if (q0 >= g.L) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t rowbase = g.headbase + (g.seg0 + g.off) * g.rs;
+  const auto rq = dev_rsrc(reinterpret_cast<const T*>(a.q) + rowbase, g.range);
+  const auto rk = dev_rsrc(reinterpret_cast<const T*>(a.k) + rowbase, g.range);
+  const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, g.range);
+  const auto rdo = dev_rsrc(reinterpret_cast<const T*>(a.dout) + rowbase, g.range);
+
+  const int32_t qw0 = q0 + 32 * wv;  // this wave's first query
+  const int32_t mq = qw0 + n;        // this lane's query
+  RowFrag<BF> qf, df;                // B operands of S^T = K Q^T and dP^T = V dout^T
+  qf.load(rq, (uint32_t)mq * g.mbytes, hh);
+  df.load(rdo, (uint32_t)mq * g.mbytes, hh);
+  float l2 = INFINITY, dd = 0.f;
+  int64_t pos = 0;
+  if (mq < g.L) {
+    pos = g.seg0 + g.off + (int64_t)mq * g.r;
+    l2 = a.lse[g.bh * a.N + pos] * kLog2e;
+    dd = a.dvec[g.bh * a.N + pos];
+  }
+
+  f32x16 dQ[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dQ[db][v] = 0.f;
+
+  const int32_t qend_wg = min(g.L, q0 + 32 * NW);
+  const int32_t nkt = CAUSAL ? (qend_wg + BK - 1) / BK : (g.L + BK - 1) / BK;
+  const int32_t qend_w = min(g.L, qw0 + 32);
+  const int32_t nkt_w = qw0 >= g.L ? 0 : (CAUSAL ? (qend_w + BK - 1) / BK : nkt);
+
+  PairStager<BF, BK, NT> stg;
+  stg.init(tid, g.mbytes);
+  auto load_tile = [&](int t) { stg.load(rk, rv, (uint32_t)(t * BK) * g.mbytes); };
+  auto store_tile = [&](int buf) {
+    char* base = smem + buf * kBufBytes;
+    stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
+  };
+
+  const float sl2 = a.sl2;
+  const uint32_t trl = tr_lane_offset<ST>(lane);
+
+  auto compute = [&](int buf, int t) {
+    const char* base = smem + buf * kBufBytes;
+    const T* Ks = reinterpret_cast<const T*>(base);
+    const T* Vs = reinterpret_cast<const T*>(base + kTileBytes);
+#pragma unroll
+    for (int kb = 0; kb < KBT; ++kb) {
+      const int32_t kb0 = t * BK + 32 * kb;  // first key of the block
+      if (kb0 >= g.L) break;
+      if (CAUSAL && kb0 > qw0) break;  // 32-aligned: every key follows every query
+      const int row = kb * 32 + n;
+      f32x16 S, dP;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[v] = dP[v] = 0.f;
+      if constexpr (BF) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + row * ST + 16 * ks + 8 * hh);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + row * ST + 16 * ks + 8 * hh);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf.x[ks], S, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df.x[ks], dP, 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 32; ++ks) {
+          const float ka = reinterpret_cast<const float*>(Ks)[row * ST + 2 * ks + hh];
+          const float va = reinterpret_cast<const float*>(Vs)[row * ST + 2 * ks + hh];
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(ka, qf.x[ks], S, 0, 0, 0);
+          dP = __builtin_amdgcn_mfma_f32_32x32x2f32(va, df.x[ks], dP, 0, 0, 0);
+        }
+      }
+      // register v: key kb0 + 8(v/4) + 4hh + v%4, query mq
+      float sv[16];
+      const bool diag = CAUSAL && kb0 == qw0;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l2));
+        if (diag && 8 * (v >> 2) + 4 * hh + (v & 3) > n) p = 0.f;
+        sv[v] = p * (dP[v] - dd);
+      }
+      if constexpr (BF) {
+        const lds_cptr kbase = (lds_cptr)smem + buf * kBufBytes;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8 sb = to_bf16x8(sv + 8 * c);
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            const uint32_t o = trl + (uint32_t)((kb * 32 + 16 * c) * ST + db * 32) * 2;
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(kbase, o, ST), sb, dQ[db],
+                                                             0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ki = kb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            const float kv = reinterpret_cast<const float*>(Ks)[ki * ST + db * 32 + n];
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(kv, sv[v], dQ[db], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < nkt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nkt) load_tile(t + 1);
+    if (t < nkt_w) compute(buf, t);
+    if (t + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (mq >= g.L) return;
+  if (coverage(a, (uint32_t)pos, tl.h) == 1) {
+    put_row<BF>(a.dq, g.headbase + pos * g.rs, dQ, a.scale, hh);
+  } else {
+    const PatDev& P = a.pat[tl.p];
+    const int64_t prow = (g.bh * P.nseg + tl.seg) * P.lmax + mq;
+    put_partial(a.ws + P.po_off + prow * kDh, dQ, a.scale, hh);
+  }
+}
+
+// ---------------------------------------------------------------- row passes
+
+constexpr int kLanesPerRow = 4;
+constexpr int kDimsPerLane = kDh / kLanesPerRow;  // 16
+constexpr int kRowThreads = 256;
+constexpr int kRowsPerBlock = kRowThreads / kLanesPerRow;
+
+// 16 consecutive elements of a row as floats.
+template <bool BF>
+__device__ inline void load16(const void* base, int64_t elem, float* x) {
+  if constexpr (BF) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 u = p[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[8 * j + 2 * i] = __uint_as_float(u[i] << 16);
+        x[8 * j + 2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+      }
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 u = p[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * j + i] = u[i];
+    }
+  }
+}
+
+template <bool BF>
+__device__ inline void store16(void* base, int64_t elem, const float* x) {
+  if constexpr (BF) {
+    u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<__bf16*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      p[j] = u32x4{dev_pack_bf16(x[8 * j], x[8 * j + 1]), dev_pack_bf16(x[8 * j + 2], x[8 * j + 3]),
+                   dev_pack_bf16(x[8 * j + 4], x[8 * j + 5]),
+                   dev_pack_bf16(x[8 * j + 6], x[8 * j + 7])};
+  } else {
+    f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + elem);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+  }
+}
+
+// D = dout . out per row; 4 lanes per row, 16 dimensions each.
+template <bool BF>
+__global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(const BwdRowArgs a,
+                                                              const FastDiv h_div) {
+  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
+  const int sub = threadIdx.x % kLanesPerRow;
+  if (row >= (uint32_t)(a.N * a.H)) return;  // all 4 lanes of a row leave together
+  const uint32_t t = fdiv(row, h_div);
+  const int32_t h = (int32_t)(row - t * (uint32_t)a.H);
+  const int64_t b = blockIdx.y;
+  const int64_t elem = ((b * a.N + t) * a.H + h) * kDh + kDimsPerLane * sub;
+  float o[kDimsPerLane], d[kDimsPerLane];
+  load16<BF>(a.out, elem, o);
+  load16<BF>(a.dout, elem, d);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDimsPerLane; ++i) s = fmaf(o[i], d[i], s);
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  if (sub == 0) a.dvec[(b * a.H + h) * a.N + t] = s;
+}
+
+// Sum of the per-pattern partials of rows two or more patterns gather; zero
+// gradients for rows no pattern gathers. Rows one pattern gathers were
+// written by the dK/dV and dQ kernels.
+template <bool BF>
+__global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs a,
+                                                               const FastDiv h_div) {
+  const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
+  const int sub = threadIdx.x % kLanesPerRow;
+  if (row >= (uint32_t)(a.N * a.H)) return;
+  const uint32_t t = fdiv(row, h_div);
+  const int32_t h = (int32_t)(row - t * (uint32_t)a.H);
+  const int64_t b = blockIdx.y;
+
+  int32_t ci[kMaxPat];
+  int cover = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPat; ++i) {
+    ci[i] = i < a.np ? (int32_t)compact_index(t, a.pat[i], head_offset(h, a.pat[i].r)) : -1;
+    cover += ci[i] >= 0;
+  }
+  if (cover == 1) return;
+
+  float acc[3][kDimsPerLane];
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int i = 0; i < kDimsPerLane; ++i) acc[w][i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxPat; ++i) {
+    if (ci[i] < 0) continue;
+    const PatDev& P = a.pat[i];
+    const int64_t slots = P.units * P.lmax;
+    const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(a.ws + P.po_off + (w * slots + prow) * kDh +
+                                                        kDimsPerLane * sub);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 x = src[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[w][4 * j + e] += x[e];
+      }
+    }
+  }
+  const int64_t elem = ((b * a.N + t) * a.H + h) * kDh + kDimsPerLane * sub;
+  store16<BF>(a.dq, elem, acc[0]);
+  store16<BF>(a.dk, elem, acc[1]);
+  store16<BF>(a.dv, elem, acc[2]);
+}
+
+template <int NW, bool BF>
+hipError_t launch_kv_cfg(const BwdArgs& a, bool causal, int64_t grid, hipStream_t st) {
+  const dim3 g((uint32_t)grid), b(NW * 64);
+  if (causal)
+    hipLaunchKernelGGL((bwd_kv_kernel<NW, true, BF>), g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_kv_kernel<NW, false, BF>), g, b, 0, st, a);
+  return hipGetLastError();
+}
+
+template <int NW, bool BF>
+hipError_t launch_q_cfg(const BwdArgs& a, bool causal, int64_t grid, hipStream_t st) {
+  const dim3 g((uint32_t)grid), b(NW * 64);
+  if (causal)
+    hipLaunchKernelGGL((bwd_q_kernel<NW, true, BF>), g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_q_kernel<NW, false, BF>), g, b, 0, st, a);
+  return hipGetLastError();
+}
+
+dim3 row_grid(const BwdRowArgs& a) {
+  const int64_t rows = a.N * a.H;
+  return dim3((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const BwdRowArgs& a, bool bf16, hipStream_t st) {
+  const FastDiv hd = make_fastdiv((uint32_t)a.H);
+  if (bf16)
+    hipLaunchKernelGGL(bwd_prep_kernel<true>, row_grid(a), dim3(kRowThreads), 0, st, a, hd);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<false>, row_grid(a), dim3(kRowThreads), 0, st, a, hd);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
+                         hipStream_t st) {
+  if (bf16) return nw == 4 ? launch_kv_cfg<4, true>(a, causal, grid, st)
+                           : launch_kv_cfg<1, true>(a, causal, grid, st);
+  return nw == 4 ? launch_kv_cfg<4, false>(a, causal, grid, st)
+                 : launch_kv_cfg<1, false>(a, causal, grid, st);
+}
+
+hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
+                        hipStream_t st) {
+  if (bf16) return nw == 4 ? launch_q_cfg<4, true>(a, causal, grid, st)
+                           : launch_q_cfg<1, true>(a, causal, grid, st);
+  return nw == 4 ? launch_q_cfg<4, false>(a, causal, grid, st)
+                 : launch_q_cfg<1, false>(a, causal, grid, st);
+}
+
+hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st) {
+  const FastDiv hd = make_fastdiv((uint32_t)a.H);
+  if (bf16)
+    hipLaunchKernelGGL(bwd_merge_kernel<true>, row_grid(a), dim3(kRowThreads), 0, st, a, hd);
+  else
+    hipLaunchKernelGGL(bwd_merge_kernel<false>, row_grid(a), dim3(kRowThreads), 0, st, a, hd);
+  return hipGetLastError();
+}
+
+}  // namespace da

@@ -1,0 +1,55 @@
+// Parameter blocks of the backward kernels (host and device).
+#pragma once
+
+#include "da_common.hpp"
+
+namespace da {
+
+// Backward launch over every tile of every pattern. The tile order is the
+// forward's (units dealt to XCDs round-robin, patterns sorted by ntile,
+// descending); ntile counts tiles of 32 * NW gathered rows, keys for the
+// dK/dV kernel and queries for the dQ kernel.
+//
+// Partial slots: a pattern with po_off >= 0 keeps, at float offset po_off of
+// ws, three blocks of units * lmax rows of kDh floats (dq, dk, dv in that
+// order; row index ((b * H + h) * nseg + seg) * lmax + m). Rows that exactly
+// one pattern gathers bypass them and are written to dq / dk / dv directly.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;   // [B, H, N], natural log, from the forward pass
+  const float* dvec;  // [B, H, N], D = dout . out per row
+  void* dq;
+  void* dk;
+  void* dv;
+  float* ws;
+  int64_t B;
+  int64_t N;
+  int32_t H;
+  int32_t np;
+  float sl2;    // softmax scale * log2(e)
+  float scale;  // softmax scale
+  PatDev pat[kMaxPat];
+  int64_t unit_start[kMaxPat + 1];
+};
+
+// Row-wise passes of the backward (D, and the partial sums): per (batch,
+// position, head) row.
+struct BwdRowArgs {
+  const void* out;
+  const void* dout;
+  float* dvec;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* ws;
+  int64_t B;
+  int64_t N;
+  int32_t H;
+  int32_t np;
+  PatDev pat[kMaxPat];  // caller's order
+};
+
+}  // namespace da

@@ -2,6 +2,7 @@
 // and merge_kernel.hip). All launches are asynchronous on the given stream.
 #pragma once
 
+#include "da_bwd.hpp"
 #include "da_common.hpp"
 
 namespace da {
@@ -17,6 +18,16 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, b
 
 // Log-sum-exp merge of the per-pattern partials into out and lse.
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st);
+
+// Backward pass (bwd_kernel.hip): D = dout . out per row; dK and dV per
+// key tile; dQ per query tile (tiles of 32 * nw gathered rows, the
+// attention launch's tile order and grid); the partial sums and zero rows.
+hipError_t launch_bwd_prep(const BwdRowArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
+                         hipStream_t st);
+hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
+                        hipStream_t st);
+hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st);
 
 // Test hooks: dump the gather map / the inverse (coverage) map of one
 // pattern for one head, computed with the kernels' own index functions.

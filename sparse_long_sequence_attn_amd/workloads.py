@@ -12,7 +12,9 @@ Recipe (all q, k, v are [B, N, H, Dh], Dh = 64):
     even; both the GPU and the oracle consume the rounded values.
 The million-token workload is drawn on the GPU with torch's generator
 instead (12 GB of host float32 would be needed otherwise); the oracle then
-reads back the exact bf16 bits it checks.
+reads back the exact bf16 bits it checks. The backward pass's output
+gradient dout comes from a PCG64 stream of its own (workload seed + 100000),
+drawn and rounded the same way.
 """
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
@@ -121,6 +123,23 @@ def host_inputs(w: Workload):
     if w.dtype == "f32":
         return q, k, v
     return bf16_round_bits(q), bf16_round_bits(k), bf16_round_bits(v)
+
+
+# Offset between a workload's seed and the seed of its output gradient.
+DOUT_SEED_OFFSET = 100_000
+
+
+def grad_output(B, N, H, Dh, dtype, seed):
+    """The gradient dout of the loss with respect to the output, for the
+    backward pass: float32 standard normals of shape [B, N, H, Dh] from a
+    PCG64 generator of its own, rounded to bf16 bits for bf16."""
+    d = np.random.default_rng(seed).standard_normal((B, N, H, Dh), dtype=np.float32)
+    return d if dtype == "f32" else bf16_round_bits(d)
+
+
+def workload_grad_output(w: Workload):
+    """dout of a workload (seed = workload seed + DOUT_SEED_OFFSET)."""
+    return grad_output(w.B, w.N, w.H, w.Dh, w.dtype, w.seed + DOUT_SEED_OFFSET)
 
 
 def random_inputs(B, N, H, Dh, dtype, seed, q_scale=1.0):

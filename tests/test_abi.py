@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_native.SIGNATURES)
@@ -46,6 +46,9 @@ def test_exports_every_declared_function(lib):
 def test_binding_constants_match_header():
     c = header_constants()
     assert c["DA_F32"] == _native.DA_F32 and c["DA_BF16"] == _native.DA_BF16
+    for name in ("DA_BWD_PREP", "DA_BWD_KV", "DA_BWD_Q", "DA_BWD_MERGE", "DA_BWD_ALL"):
+        assert c[name] == getattr(_native, name)
+    assert c["DA_BWD_ALL"] == c["DA_BWD_PREP"] | c["DA_BWD_KV"] | c["DA_BWD_Q"] | c["DA_BWD_MERGE"]
     for code, name in _native.ERROR_NAMES.items():
         assert c[name] == code
     text = open(HEADER).read()
@@ -142,3 +145,88 @@ def test_map_hooks_validate(lib, fn):
     assert f(64, 4, p, -1, A, 1 << 20, None) == -9
     assert f(64, 4, p, 0, A, 3, None) == -9
     assert f(64, 4, p, 0, A + 4, 1 << 20, None) == -7
+
+
+# ---------------------------------------------------------------- backward
+
+DOUT, DQ, DK, DV = (A * i for i in range(7, 11))
+
+
+def bwd(lib, stages=None, q=Q, k=K, v=V, out=OUT, lse=LSE, dout=DOUT, dq=DQ, dk=DK, dv=DV, B=1,
+        N=64, H=4, Dh=64, pats=((16, 2), (32, 4)), npat=None, causal=1, dtype=_native.DA_BF16,
+        scale=0.0, ws=WS, wsb=1 << 30):
+    arr = _native.pattern_array(pats) if pats is not None else None
+    args = (q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Dh, arr,
+            len(pats) if npat is None else npat, causal, dtype, scale, ws, wsb, None)
+    if stages is None:
+        return lib.dilated_attn_bwd(*args)
+    return lib.dilated_attn_bwd_stages(stages, *args)
+
+
+@pytest.mark.parametrize("stages", [None, 15, 1, 8])
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), -1), (dict(out=None), -1), (dict(lse=None), -1), (dict(dout=None), -1),
+    (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1), (dict(pats=None, npat=1), -1),
+    (dict(B=-1), -2), (dict(N=60), -2), (dict(N=1 << 31), -2),
+    (dict(pats=()), -3), (dict(pats=((8, 9),)), -3),
+    (dict(dtype=2), -4), (dict(Dh=128), -5),
+    (dict(ws=None), -6), (dict(wsb=100), -6), (dict(pats=((16, 2),), wsb=4), -6),
+    (dict(dout=DOUT + 8), -7), (dict(dq=DQ + 8), -7), (dict(dv=DV + 2), -7),
+    (dict(lse=LSE + 2), -7), (dict(ws=WS + 64), -7),
+    (dict(dq=Q), -8), (dict(dk=OUT), -8), (dict(dv=DOUT + 64), -8), (dict(ws=LSE), -8),
+    (dict(dq=DK), -8), (dict(dv=DK + 256), -8), (dict(ws=DQ), -8),
+    (dict(causal=2), -9), (dict(scale=math.nan), -9),
+])
+def test_bwd_invalid_calls_rejected(lib, stages, kwargs, code):
+    assert bwd(lib, stages, **kwargs) == code
+
+
+@pytest.mark.parametrize("stages", [0, 16, -1, 31])
+def test_bwd_stage_flags_validated(lib, stages):
+    assert bwd(lib, stages) == -9
+
+
+def test_bwd_inputs_may_alias_each_other(lib):
+    # q, k, v, out, dout read-only: sharing is allowed, so validation passes
+    # until the (absent) workspace check
+    assert bwd(lib, k=Q, v=Q, dout=Q, ws=None) == -6
+
+
+def test_bwd_empty_problems_are_accepted_without_launch(lib):
+    for B, N, H in [(0, 64, 4), (1, 0, 4), (1, 64, 0)]:
+        assert bwd(lib, B=B, N=N, H=H, q=None, k=None, v=None, out=None, lse=None, dout=None,
+                   dq=None, dk=None, dv=None, ws=None, wsb=0) == 0
+
+
+def bwd_ws_expected(B, N, H, pats):
+    """Backward workspace from the documented layout: a float D per row
+    (rounded up to 256 bytes), then for two or more patterns three float
+    partial rows (dq, dk, dv) per gathered row slot, per pattern rounded up
+    to 256 bytes."""
+    tot = -(-B * H * N * 4 // 256) * 256
+    if len(pats) > 1:
+        for (w, r) in pats:
+            wp = min(w, N)
+            rows = B * H * (N // wp) * (-(-wp // r))
+            tot += -(-3 * rows * 64 * 4 // 256) * 256
+    return tot
+
+
+@pytest.mark.parametrize("B,N,H,pats", [
+    (1, 512, 8, [(64, 2)]),
+    (4, 8192, 12, [(2048, 1), (4096, 2), (8192, 4)]),
+    (1, 32768, 16, [(2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12)]),
+    (2, 96, 3, [(1000, 7), (8, 1), (96, 96)]),
+])
+def test_bwd_workspace_bytes(B, N, H, pats):
+    got = _native.bwd_workspace_bytes(B, N, H, 64, pats, _native.DA_BF16)
+    assert got == bwd_ws_expected(B, N, H, pats)
+
+
+def test_bwd_workspace_bytes_errors(lib):
+    out = ctypes.c_size_t(0)
+    arr = _native.pattern_array([(16, 2)])
+    assert lib.dilated_attn_bwd_workspace_bytes(1, 64, 4, 64, arr, 1, 1, None) == -1
+    assert lib.dilated_attn_bwd_workspace_bytes(1, 60, 4, 64, arr, 1, 1, ctypes.byref(out)) == -2
+    assert lib.dilated_attn_bwd_workspace_bytes(0, 64, 4, 64, arr, 1, 1, ctypes.byref(out)) == 0
+    assert out.value == 0
