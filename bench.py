@@ -1,18 +1,23 @@
-"""Benchmark of the dilated-attention forward pass on one MI355X.
+"""Benchmark of the dilated-attention forward (default) or backward pass on
+one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+                    [--pass fwd|bwd]
 
-A step is one whole forward pass (the attention kernel over every pattern,
-then the log-sum-exp merge) on inputs already resident in GPU memory. W
-untimed steps run first; K steps are then timed between two device
-synchronisations. Inside the timed region HIP events on the launch stream
-bracket the attention kernel of every step, which gives its average launch
-duration for the roofline figure.
+Forward: a step is one whole forward pass (the attention kernel over every
+pattern, then the log-sum-exp merge). Backward (--pass bwd): a step is one
+whole backward pass (D = dout . out, the dK/dV kernel, the dQ kernel, the
+partial sums), given the forward pass's out and lse. Inputs are resident in
+GPU memory. W untimed steps run first; K steps are then timed between two
+device synchronisations. Inside the timed region HIP events on the launch
+stream bracket every kernel of every step, which gives each kernel's
+average launch duration for the roofline figure.
 
 Prints one JSON line. `value` is tokens/s (B * N / step time). `roofline`
-reports the attention kernel against the bf16 MFMA peak using the
-algorithmic FLOP count; `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload on this host's cores.
+reports the dominant kernel (the attention kernel; for the backward pass
+the dK/dV kernel) against the bf16 MFMA peak using the algorithmic FLOP
+count; `cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload on this host's cores.
 """
 import argparse
 import hashlib
@@ -25,27 +30,34 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "dilated-attention fwd tokens/sec and % bf16 MFMA peak at N=32K, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_fwd_paper_mixture_n32768.json")
-KERNEL_SOURCES = ["attn_kernel.hip", "da_common.hpp"]
+METRIC_BWD = "dilated-attention bwd tokens/sec and % bf16 MFMA peak at N=32K, 1 GPU"
+TRAFFIC = {
+    "fwd": (os.path.join(ROOT, "profiles", "traffic_attn_fwd_paper_mixture_n32768.json"),
+            ["attn_kernel.hip", "da_common.hpp"]),
+    "bwd": (os.path.join(ROOT, "profiles", "traffic_bwd_kv_paper_mixture_n32768.json"),
+            ["bwd_kernel.hip", "da_common.hpp", "da_bwd.hpp", "da_device.hpp"]),
+}
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "sparse_long_sequence_attn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, or None when there is none or the kernel changed since."""
+def measured_traffic(which, workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel's
+    sources changed since."""
+    path, sources = TRAFFIC[which]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("source_sha256") != kernel_source_hash():
+    if t.get("workload") != workload or t.get("source_sha256") != kernel_source_hash(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -74,6 +86,119 @@ def cpu_baseline(w, heads):
     }
 
 
+def cpu_baseline_bwd(w, heads):
+    """The oracle's backward pass (as it stands) on the first `heads` heads."""
+    import numpy as np
+
+    import oracle
+    from sparse_long_sequence_attn_amd.workloads import host_inputs, workload_grad_output
+
+    q, k, v = host_inputs(w)
+    d = workload_grad_output(w)
+    q, k, v, d = (np.ascontiguousarray(x[:, :, :heads]) for x in (q, k, v, d))
+    t0 = time.perf_counter()
+    oracle.bwd(q, k, v, d, w.patterns, causal=w.causal)
+    dt = time.perf_counter() - t0
+    full = dt * w.H / heads
+    return {
+        "value": w.tokens / full,
+        "unit": "tokens/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"backward, heads 0-{heads - 1} of {w.H} of the same workload (all "
+                  f"{w.B * w.N} tokens, all patterns), fp64 C oracle, {dt:.2f} s measured, "
+                  f"scaled by {w.H}/{heads}",
+    }
+
+
+def run_bwd(args, w, dev, q, k, v):
+    import torch
+
+    from sparse_long_sequence_attn_amd import (DA_BWD_KV, DA_BWD_MERGE, DA_BWD_PREP, DA_BWD_Q,
+                                               BwdProblem, Problem)
+    from sparse_long_sequence_attn_amd.costs import bwd_cost, peak_tflops
+    from sparse_long_sequence_attn_amd.workloads import to_torch, workload_grad_output
+
+    if w.device_generated:
+        g = torch.Generator(device=dev)
+        g.manual_seed(w.seed + 100_000)
+        dout = torch.randn(q.shape, generator=g, device=dev, dtype=torch.float32).to(q.dtype)
+    else:
+        dout = to_torch(workload_grad_output(w), dev)
+    fwd = Problem(q, k, v, w.patterns, w.causal)
+    fwd.run()
+    bp = BwdProblem(q, k, v, fwd.out, fwd.lse, dout, w.patterns, w.causal)
+    stream = torch.cuda.current_stream(dev)
+    stages = (DA_BWD_PREP, DA_BWD_KV, DA_BWD_Q, DA_BWD_MERGE)
+    for _ in range(args.warmup):
+        for st in stages:
+            bp.run(st, stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        for j, st in enumerate(stages):
+            bp.run(st, stream)
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    names = ["prep", "kv", "q", "merge"]
+    kms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / K for j, n in enumerate(names)}
+
+    c = bwd_cost(w.B, w.N, w.H, w.Dh, w.patterns, w.causal, 2 if w.dtype == "bf16" else 4)
+    peak = peak_tflops(w.dtype)
+    kv_tflops = c.flops_kv / (kms["kv"] / 1e3) / 1e12
+    q_tflops = c.flops_q / (kms["q"] / 1e3) / 1e12
+    step_tflops = c.flops_alg / (ms_step / 1e3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(kv_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(kv_tflops / peak, 4), "traffic": measured_traffic("bwd", w.name),
+            "kernel": "bwd_kv_kernel", "kernel_ms": round(kms["kv"], 4)}
+    result = {
+        "metric": METRIC_BWD,
+        "value": round(w.tokens / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded normal q, k, v, dout; see workloads.py)",
+        "config": {"workload": w.name, "pass": "bwd", "B": w.B, "N": w.N, "H": w.H, "Dh": w.Dh,
+                   "patterns": [list(p) for p in w.patterns], "causal": w.causal,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "single GPU"},
+        "roofline": roof,
+        "detail": {
+            "kernel_ms": {n: round(x, 4) for n, x in kms.items()},
+            "tflops_kv_kernel": round(kv_tflops, 2),
+            "tflops_q_kernel": round(q_tflops, 2),
+            "pct_bf16_peak_q_kernel": round(100 * q_tflops / peak, 2),
+            "tflops_algorithmic_step": round(step_tflops, 2),
+            "pct_bf16_peak_algorithmic_step": round(100 * step_tflops / peak, 2),
+            "flops_algorithmic": c.flops_alg,
+            "flops_kv_kernel": c.flops_kv,
+            "flops_q_kernel": c.flops_q,
+            "gbs_prep": round(c.prep_bytes / (kms["prep"] / 1e3) / 1e9, 1),
+            "gbs_merge": round(c.merge_bytes / (kms["merge"] / 1e3) / 1e9, 1)
+            if c.merge_bytes > 0 else None,
+            "kv_algorithmic_bytes": c.kv_bytes,
+            "q_algorithmic_bytes": c.q_bytes,
+            "device": torch.cuda.get_device_name(dev),
+        },
+    }
+    if not args.no_cpu_baseline and not w.device_generated:
+        result["cpu_baseline"] = cpu_baseline_bwd(w, min(args.cpu_heads, w.H))
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +208,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed region, run one device copy of this many MiB "
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
@@ -105,6 +231,9 @@ def main():
         q, k, v = device_inputs(w)
     else:
         q, k, v = (to_torch(x, dev) for x in host_inputs(w))
+    if args.which == "bwd":
+        run_bwd(args, w, dev, q, k, v)
+        return
     prob = Problem(q, k, v, w.patterns, w.causal)
     stream = torch.cuda.current_stream(dev)
 
@@ -154,7 +283,7 @@ def main():
         gbs = c.attn_bytes / (attn_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = measured_traffic(w.name)
+    roof["traffic"] = measured_traffic("fwd", w.name)
     roof["kernel"] = "attn_fwd_kernel"
     roof["kernel_ms"] = round(attn_ms, 4)
 

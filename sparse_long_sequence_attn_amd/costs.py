@@ -100,6 +100,54 @@ def cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causal: b
     return Cost(flops_alg, flops_ns, exps, rows, attn_read, attn_write, merge_read, merge_write)
 
 
+@dataclass
+class BwdCost:
+    pairs: float            # useful (query, key) pairs, summed over patterns
+    flops_alg: float        # five products per pair (S recomputed, dP, dV, dK, dQ): 10 Dh
+    flops_kv: float         # the dK/dV kernel's products (S, dP, dV, dK): 8 Dh per pair
+    flops_q: float          # the dQ kernel's products (S, dP, dQ): 6 Dh per pair
+    exps: float             # exponentials, once per pair in each of the two kernels
+    prep_bytes: float       # out and dout read, D written
+    kv_bytes: float         # gathered q, k, v, dout rows + lse, D read; dk, dv written
+    q_bytes: float          # gathered q, k, v, dout rows + lse, D read; dq written
+    merge_bytes: float      # partials read, sums and zero rows written
+
+
+def bwd_cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causal: bool = True,
+             elem_bytes: int = 2) -> BwdCost:
+    """Work and compulsory HBM traffic of one backward call.
+
+    Each gathered row of each pattern is read once by each of the two main
+    kernels (q, k, v, dout rows plus its lse and D); rows one pattern
+    gathers are written once as final gradients, rows several patterns
+    gather once per covering pattern as fp32 partials (Dh floats per
+    gradient), which the merge kernel reads back before writing the sums
+    and the zero rows of positions no pattern gathers."""
+    fwd = cost(B, N, H, Dh, patterns, causal, elem_bytes)
+    pairs = fwd.flops_alg / (4.0 * Dh)
+    rows = fwd.gathered_rows
+    row = Dh * elem_bytes
+    prow = Dh * 4.0
+    t = np.arange(N, dtype=np.int64)
+    single = multi_slots = multi_rows = none = 0
+    for h in range(H):
+        count = np.zeros(N, dtype=np.int64)
+        for (w, r) in patterns:
+            wp = min(w, N)
+            count += ((t % wp) % r) == (h % r)
+        single += int((count == 1).sum())
+        none += int((count == 0).sum())
+        multi_rows += int((count >= 2).sum())
+        multi_slots += int(count[count >= 2].sum())
+    reads = rows * (4.0 * row + 8.0)
+    kv_write = B * (single * 2.0 * row + multi_slots * 2.0 * prow)
+    q_write = B * (single * row + multi_slots * prow)
+    merge = B * (multi_slots * 3.0 * prow + (multi_rows + none) * 3.0 * row)
+    prep = B * N * H * (2.0 * row + 4.0)
+    return BwdCost(pairs, 10.0 * Dh * pairs, 8.0 * Dh * pairs, 6.0 * Dh * pairs, 2.0 * pairs,
+                   prep, reads + kv_write, reads + q_write, merge)
+
+
 # MI355X published peaks (dense)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_MFMA_TFLOPS = 157.3
