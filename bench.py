@@ -2,12 +2,15 @@
 one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
-                    [--pass fwd|bwd]
+                    [--pass fwd|bwd|module]
 
 Forward: a step is one whole forward pass (the attention kernel over every
 pattern, then the log-sum-exp merge). Backward (--pass bwd): a step is one
 whole backward pass (D = dout . out, the dK/dV kernel, the dQ kernel, the
-partial sums), given the forward pass's out and lse. Inputs are resident in
+partial sums), given the forward pass's out and lse. Module (--pass module):
+a step is one training step of the DilatedAttention module (projections,
+qk_norm, attention, output projection; forward, then backward into x and
+every parameter) at the README's usage shape. Inputs are resident in
 GPU memory. W untimed steps run first; K steps are then timed between two
 device synchronisations. Inside the timed region HIP events on the launch
 stream bracket every kernel of every step, which gives each kernel's
@@ -199,6 +202,117 @@ def run_bwd(args, w, dev, q, k, v):
     print(json.dumps(result), flush=True)
 
 
+MODULE_CONFIG = {"workload": "readme_module_b32_n8192_d512_h8_w64r2_qknorm_bf16", "B": 32,
+                 "N": 8192, "dim": 512, "heads": 8, "segment_size": 64, "dilation_rate": 2,
+                 "qk_norm": True, "causal": True, "seed": 400}
+METRIC_MODULE = "DilatedAttention module fwd+bwd tokens/sec, README usage shape, 1 GPU"
+
+
+def run_module(args, dev):
+    """One training step of the DilatedAttention module (forward, then
+    backward into x and every parameter) at the README's usage shape."""
+    import torch
+
+    from sparse_long_sequence_attn_amd.costs import PEAK_HBM_GBS, bwd_cost, cost
+    from sparse_long_sequence_attn_amd.module import DilatedAttention
+    from sparse_long_sequence_attn_amd.workloads import module_params, module_x
+
+    c = MODULE_CONFIG
+    B, N, dim, heads = c["B"], c["N"], c["dim"], c["heads"]
+    mod = DilatedAttention(dim, heads, c["dilation_rate"], c["segment_size"], qk_norm=c["qk_norm"],
+                           causal=c["causal"], device=dev, dtype=torch.bfloat16)
+    named = dict(mod.named_parameters())
+    names = {"wq": "to_q.weight", "wk": "to_k.weight", "wv": "to_v.weight", "wo": "to_out.weight",
+             "q_gain": "q_norm.weight", "q_bias": "q_norm.bias", "k_gain": "k_norm.weight",
+             "k_bias": "k_norm.bias"}
+    with torch.no_grad():
+        for k, v in module_params(dim, heads, c["qk_norm"], False, c["seed"]).items():
+            if v is not None:
+                named[names[k]].copy_(torch.from_numpy(v))
+    x = torch.from_numpy(module_x(B, N, dim, c["seed"] + 1)).to(dev, torch.bfloat16)
+    x.requires_grad_()
+    dy = torch.from_numpy(module_x(B, N, dim, c["seed"] + 2)).to(dev, torch.bfloat16)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mod.zero_grad(set_to_none=True)
+        x.grad = None
+        mod(x).backward(dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / K
+
+    # the library's kernels on the step's own shapes, timed alone
+    from sparse_long_sequence_attn_amd import DA_BWD_KV, DA_BWD_MERGE, DA_BWD_PREP, DA_BWD_Q
+    from sparse_long_sequence_attn_amd import BwdProblem, Problem
+
+    with torch.no_grad():
+        shape = (B, N, heads, 64)
+        q = mod.q_norm(mod.to_q(x).view(shape)).contiguous()
+        k = mod.k_norm(mod.to_k(x).view(shape)).contiguous()
+        v = mod.to_v(x).view(shape).contiguous()
+    pats = list(mod.patterns)
+    fp = Problem(q, k, v, pats)
+    fp.run()
+    bp = BwdProblem(q, k, v, fp.out, fp.lse, torch.randn_like(q), pats)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(3):
+        fp.attention_stage(stream)
+        bp.run(DA_BWD_PREP | DA_BWD_KV | DA_BWD_Q | DA_BWD_MERGE, stream)
+    reps = max(K, 10)
+    ev[0].record(stream)
+    for _ in range(reps):
+        fp.attention_stage(stream)
+    ev[1].record(stream)
+    for _ in range(reps):
+        bp.run(DA_BWD_PREP | DA_BWD_KV | DA_BWD_Q | DA_BWD_MERGE, stream)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    attn_ms = ev[0].elapsed_time(ev[1]) / reps
+    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
+    fc = cost(B, N, heads, 64, pats, c["causal"], 2)
+    bc = bwd_cost(B, N, heads, 64, pats, c["causal"], 2)
+    gbs = fc.attn_bytes / (attn_ms / 1e3) / 1e9
+    proj_flops = 2.0 * B * N * dim * dim * 4 * 3  # four projections, forward + two backward GEMMs
+    result = {
+        "metric": METRIC_MODULE,
+        "value": round(B * N / (ms_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal x, dy and weights; see workloads.py)",
+        "config": dict(c, **{"pass": "module fwd+bwd", "global_batch": B, "seq_len": N,
+                             "parallelism": "single GPU"}),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "attn_fwd_kernel (on the module's q, k, v)",
+                     "kernel_ms": round(attn_ms, 4)},
+        "detail": {
+            "attention_fwd_ms": round(attn_ms, 4),
+            "attention_bwd_ms": round(bwd_ms, 4),
+            "attention_share_of_step": round((attn_ms + bwd_ms) / ms_step, 4),
+            "attention_bwd_algorithmic_bytes": bc.kv_bytes + bc.q_bytes + bc.prep_bytes +
+            bc.merge_bytes,
+            "projection_gemm_flops": proj_flops,
+            "device": torch.cuda.get_device_name(dev),
+        },
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,7 +322,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "module"], default="fwd")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed region, run one device copy of this many MiB "
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
@@ -224,9 +338,12 @@ def main():
     from sparse_long_sequence_attn_amd.costs import PEAK_HBM_GBS, cost, peak_tflops
     from sparse_long_sequence_attn_amd.workloads import WORKLOADS, device_inputs, host_inputs, to_torch
 
-    w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.which == "module":
+        run_module(args, dev)
+        return
+    w = WORKLOADS[args.workload]
     if w.device_generated:
         q, k, v = device_inputs(w)
     else:

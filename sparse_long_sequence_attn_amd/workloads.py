@@ -142,6 +142,32 @@ def workload_grad_output(w: Workload):
     return grad_output(w.B, w.N, w.H, w.Dh, w.dtype, w.seed + DOUT_SEED_OFFSET)
 
 
+def module_params(dim, heads, qk_norm, bias, seed):
+    """Parameters of the DilatedAttention module, float32: the four
+    projection weights [dim, dim] (out-features first) drawn N(0, 1/dim),
+    optional biases N(0, 0.01), and with qk_norm the layer-norm gains
+    1 + N(0, 0.01) and biases N(0, 0.01) over the 64 head values; one PCG64
+    stream in that order."""
+    rng = np.random.default_rng(seed)
+    p = {}
+    for n in ("wq", "wk", "wv", "wo"):
+        p[n] = (rng.standard_normal((dim, dim), dtype=np.float32) / np.float32(np.sqrt(dim)))
+    for n in ("bq", "bk", "bv", "bo"):
+        p[n] = (rng.standard_normal(dim, dtype=np.float32) * np.float32(0.1)) if bias else None
+    if qk_norm:
+        Dh = dim // heads
+        for n in ("q_gain", "k_gain"):
+            p[n] = np.float32(1.0) + np.float32(0.1) * rng.standard_normal(Dh, dtype=np.float32)
+        for n in ("q_bias", "k_bias"):
+            p[n] = np.float32(0.1) * rng.standard_normal(Dh, dtype=np.float32)
+    return p
+
+
+def module_x(B, N, dim, seed):
+    """Module input x [B, N, dim]: float32 standard normals."""
+    return np.random.default_rng(seed).standard_normal((B, N, dim), dtype=np.float32)
+
+
 def random_inputs(B, N, H, Dh, dtype, seed, q_scale=1.0):
     """Ad-hoc shapes for tests: same recipe as host_inputs()."""
     q, k, v = generate_f32(B, N, H, Dh, seed, q_scale)
