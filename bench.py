@@ -253,10 +253,12 @@ def run_module(args, dev):
     from sparse_long_sequence_attn_amd import DA_BWD_KV, DA_BWD_MERGE, DA_BWD_PREP, DA_BWD_Q
     from sparse_long_sequence_attn_amd import BwdProblem, Problem
 
+    from sparse_long_sequence_attn_amd import qk_norm_fwd
+
     with torch.no_grad():
         shape = (B, N, heads, 64)
-        q = mod.q_norm(mod.to_q(x).view(shape)).contiguous()
-        k = mod.k_norm(mod.to_k(x).view(shape)).contiguous()
+        q, k = qk_norm_fwd(mod.to_q(x).view(shape), mod.to_k(x).view(shape), mod.q_norm.weight,
+                           mod.q_norm.bias, mod.k_norm.weight, mod.k_norm.bias, mod.q_norm.eps)
         v = mod.to_v(x).view(shape).contiguous()
     pats = list(mod.patterns)
     fp = Problem(q, k, v, pats)

@@ -180,6 +180,40 @@ int dilated_attn_bwd_stages(int32_t stages, const void* q, const void* k, const 
                             int32_t dtype, float scale, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/* ------------------------------------------------------------------ qk_norm
+ *
+ * The DilatedAttention module's optional query-key normalisation (LongNet
+ * package README, DilatedAttention parameter qk_norm): every row of
+ * Dh = DA_HEAD_DIM query values and every row of key values is layer-
+ * normalised, y = (x - mean) / sqrt(var + eps) * gain + bias, with the
+ * biased variance over the row and one gain and bias vector (Dh values
+ * each) per tensor, shared by all heads.
+ *
+ * xq, xk, yq, yk, dyq, dyk, dxq, dxk: rows x Dh contiguous device arrays
+ * (e.g. [B, N, H, Dh], rows = B * N * H) of `dtype`; gains and biases: Dh
+ * values of `dtype`. All 16-byte aligned. Outputs must not overlap any
+ * input or each other (DA_ERR_ALIAS). eps must be finite and > 0
+ * (DA_ERR_ARG). rows = 0 is a no-op. */
+int dilated_attn_qk_norm_fwd(const void* xq, const void* xk, const void* gain_q,
+                             const void* bias_q, const void* gain_k, const void* bias_k, void* yq,
+                             void* yk, int64_t rows, int32_t Dh, int32_t dtype, float eps,
+                             void* stream);
+
+/* Device workspace bytes dilated_attn_qk_norm_bwd needs for `rows` rows
+ * (per-block partial sums of the gain and bias gradients). */
+int dilated_attn_qk_norm_workspace_bytes(int64_t rows, size_t* bytes);
+
+/* Backward of dilated_attn_qk_norm_fwd: dxq, dxk (rows x Dh, dtype) and
+ * dparams, a device float array [2][2][Dh]: [0][0] dgain_q, [0][1] dbias_q,
+ * [1][0] dgain_k, [1][1] dbias_k (4-byte aligned, every element written).
+ * The row statistics are recomputed from xq and xk. workspace: at least
+ * dilated_attn_qk_norm_workspace_bytes(rows), 256-byte aligned. The sums
+ * over rows are taken in a fixed order: results are deterministic. */
+int dilated_attn_qk_norm_bwd(const void* xq, const void* xk, const void* dyq, const void* dyk,
+                             const void* gain_q, const void* gain_k, void* dxq, void* dxk,
+                             float* dparams, int64_t rows, int32_t Dh, int32_t dtype, float eps,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Test hook: the gather map the kernels use, written by a device kernel
  * through the same index function as the attention kernel.
  * dev_out: device int64 [N / min(w, N)][ceil(min(w, N) / r)], segment-major;

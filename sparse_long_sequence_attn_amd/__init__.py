@@ -18,7 +18,7 @@ __all__ = [
     "coverage_map", "workspace_bytes", "strerror", "version", "load_library", "DilatedAttnError",
     "DA_F32", "DA_BF16", "DA_HEAD_DIM", "DA_MAX_PATTERNS", "Problem", "dilated_attn_bwd",
     "BwdProblem", "bwd_workspace_bytes", "DA_BWD_PREP", "DA_BWD_KV", "DA_BWD_Q", "DA_BWD_MERGE",
-    "DA_BWD_ALL",
+    "DA_BWD_ALL", "qk_norm_fwd", "qk_norm_bwd",
 ]
 
 
@@ -195,3 +195,56 @@ def gather_map(N, H, pattern, h, device="cuda"):
 def coverage_map(N, H, pattern, h, device="cuda"):
     """Device dump of the inverse map: int64 [N], compact index or -1."""
     return _map("dilated_attn_coverage_map", N, H, pattern, h, int(N), device)
+
+
+def _check_rows(name, t, like):
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor; no CPU path exists")
+    if not t.is_contiguous() or t.dtype != like.dtype or t.device != like.device:
+        raise ValueError(f"{name} must be contiguous with q's dtype and device")
+
+
+def qk_norm_fwd(xq, xk, gain_q, bias_q, gain_k, bias_k, eps=1e-5, yq=None, yk=None):
+    """Layer norm of every 64-value row of xq and xk ([..., 64]); see
+    include/dilated_attn.h. Returns (yq, yk)."""
+    import torch
+
+    for n, t in (("xk", xk), ("gain_q", gain_q), ("bias_q", bias_q), ("gain_k", gain_k),
+                 ("bias_k", bias_k)):
+        _check_rows(n, t, xq)
+    _check_rows("xq", xq, xq)
+    if xq.shape != xk.shape or xq.shape[-1] != DA_HEAD_DIM:
+        raise ValueError("xq and xk must share a shape ending in 64")
+    yq = torch.empty_like(xq) if yq is None else yq
+    yk = torch.empty_like(xk) if yk is None else yk
+    rows = xq.numel() // DA_HEAD_DIM
+    code = load_library().dilated_attn_qk_norm_fwd(
+        xq.data_ptr(), xk.data_ptr(), gain_q.data_ptr(), bias_q.data_ptr(), gain_k.data_ptr(),
+        bias_k.data_ptr(), yq.data_ptr(), yk.data_ptr(), rows, DA_HEAD_DIM, _dtype_code(xq),
+        float(eps), torch.cuda.current_stream(xq.device).cuda_stream)
+    _native.check(code, "dilated_attn_qk_norm_fwd")
+    return yq, yk
+
+
+def qk_norm_bwd(xq, xk, dyq, dyk, gain_q, gain_k, eps=1e-5):
+    """Backward of qk_norm_fwd. Returns (dxq, dxk, dparams) with dparams a
+    float32 [2, 2, 64] tensor: [q|k][gain|bias]."""
+    import torch
+
+    for n, t in (("xk", xk), ("dyq", dyq), ("dyk", dyk), ("gain_q", gain_q), ("gain_k", gain_k)):
+        _check_rows(n, t, xq)
+    _check_rows("xq", xq, xq)
+    rows = xq.numel() // DA_HEAD_DIM
+    dxq, dxk = torch.empty_like(xq), torch.empty_like(xk)
+    dparams = torch.empty((2, 2, DA_HEAD_DIM), dtype=torch.float32, device=xq.device)
+    ws = torch.empty(max(_native.qk_norm_workspace_bytes(rows), 1), dtype=torch.uint8,
+                     device=xq.device)
+    code = load_library().dilated_attn_qk_norm_bwd(
+        xq.data_ptr(), xk.data_ptr(), dyq.data_ptr(), dyk.data_ptr(), gain_q.data_ptr(),
+        gain_k.data_ptr(), dxq.data_ptr(), dxk.data_ptr(), dparams.data_ptr(), rows, DA_HEAD_DIM,
+        _dtype_code(xq), float(eps), ws.data_ptr(), ws.numel(),
+        torch.cuda.current_stream(xq.device).cuda_stream)
+    _native.check(code, "dilated_attn_qk_norm_bwd")
+    return dxq, dxk, dparams

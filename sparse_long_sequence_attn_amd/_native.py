@@ -45,6 +45,10 @@ SIGNATURES = {
                                           ctypes.POINTER(_SZ)], ctypes.c_int),
     "dilated_attn_bwd": (_BWD_ARGS, ctypes.c_int),
     "dilated_attn_bwd_stages": ([_I32] + _BWD_ARGS, ctypes.c_int),
+    "dilated_attn_qk_norm_fwd": ([_P] * 8 + [_I64, _I32, _I32, ctypes.c_float, _P], ctypes.c_int),
+    "dilated_attn_qk_norm_workspace_bytes": ([_I64, ctypes.POINTER(_SZ)], ctypes.c_int),
+    "dilated_attn_qk_norm_bwd": ([_P] * 9 + [_I64, _I32, _I32, ctypes.c_float, _P, _SZ, _P],
+                                 ctypes.c_int),
     "dilated_attn_gather_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, _P], ctypes.c_int),
     "dilated_attn_coverage_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, _P], ctypes.c_int),
     "dilated_attn_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -114,4 +118,11 @@ def bwd_workspace_bytes(B, N, H, Dh, patterns, dtype):
                                                            len(patterns), dtype,
                                                            ctypes.byref(out))
     check(code, "dilated_attn_bwd_workspace_bytes")
+    return out.value
+
+
+def qk_norm_workspace_bytes(rows):
+    out = _SZ(0)
+    check(load_library().dilated_attn_qk_norm_workspace_bytes(rows, ctypes.byref(out)),
+          "dilated_attn_qk_norm_workspace_bytes")
     return out.value

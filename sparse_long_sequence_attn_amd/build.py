@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdilated_attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "attn_kernel.hip", "merge_kernel.hip", "bwd_kernel.hip"]
+SOURCES = ["api.hip", "attn_kernel.hip", "merge_kernel.hip", "bwd_kernel.hip",
+           "qknorm_kernel.hip"]
 HEADERS = ["da_common.hpp", "kernels.hpp"]
 ARCH = "gfx950"
 

@@ -344,6 +344,16 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
+// ---------------------------------------------------------------- qk_norm
+
+int qk_norm_check(int64_t rows, int32_t Dh, int32_t dtype, float eps) {
+  if (dtype != DA_F32 && dtype != DA_BF16) return DA_ERR_DTYPE;
+  if (Dh != DA_HEAD_DIM) return DA_ERR_HEADDIM;
+  if (rows < 0 || rows > ((int64_t)1 << 40)) return DA_ERR_SHAPE;
+  if (!isfinite(eps) || !(eps > 0.f)) return DA_ERR_ARG;
+  return DA_OK;
+}
+
 // Geometry of one pattern for the map hooks.
 int map_pattern(int64_t N, int32_t H, da_pattern p, int32_t h, PatDev* out) {
   if (N < 1 || N > kMaxGrid || H < 1) return DA_ERR_SHAPE;
@@ -431,6 +441,98 @@ int dilated_attn_bwd_stages(int32_t stages, const void* q, const void* k, const 
                             void* stream) {
   return bwd_common(stages, q, k, v, out, lse, dout, dq, dk, dv, B, N, H, Dh, patterns,
                     n_patterns, causal, dtype, scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_qk_norm_workspace_bytes(int64_t rows, size_t* bytes) {
+  if (!bytes) return DA_ERR_NULL;
+  if (rows < 0) return DA_ERR_SHAPE;
+  *bytes = rows == 0 ? 0 : (size_t)(2 * da::qk_norm_blocks(rows) * 2 * kDh) * sizeof(float);
+  return DA_OK;
+}
+
+int dilated_attn_qk_norm_fwd(const void* xq, const void* xk, const void* gain_q,
+                             const void* bias_q, const void* gain_k, const void* bias_k, void* yq,
+                             void* yk, int64_t rows, int32_t Dh, int32_t dtype, float eps,
+                             void* stream) {
+  int rc = qk_norm_check(rows, Dh, dtype, eps);
+  if (rc != DA_OK || rows == 0) return rc;
+  const void* ptrs[8] = {xq, xk, gain_q, bias_q, gain_k, bias_k, yq, yk};
+  for (const void* p : ptrs) {
+    if (!p) return DA_ERR_NULL;
+    if (((uintptr_t)p & 15) != 0) return DA_ERR_ALIGN;
+  }
+  const size_t tb = (size_t)rows * kDh * (dtype == DA_BF16 ? 2 : 4);
+  const size_t pb = (size_t)kDh * (dtype == DA_BF16 ? 2 : 4);
+  const void* ins[6] = {xq, xk, gain_q, bias_q, gain_k, bias_k};
+  const size_t isz[6] = {tb, tb, pb, pb, pb, pb};
+  for (const void* o : {(const void*)yq, (const void*)yk})
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(o, tb, ins[j], isz[j])) return DA_ERR_ALIAS;
+  if (overlaps(yq, tb, yk, tb)) return DA_ERR_ALIAS;
+  da::QkNormArgs a;
+  memset(&a, 0, sizeof a);
+  a.xq = xq;
+  a.xk = xk;
+  a.yq = yq;
+  a.yk = yk;
+  a.gq = gain_q;
+  a.bq = bias_q;
+  a.gk = gain_k;
+  a.bk = bias_k;
+  a.rows = rows;
+  a.eps = eps;
+  const hipError_t e =
+      da::launch_qk_norm_fwd(a, dtype == DA_BF16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+int dilated_attn_qk_norm_bwd(const void* xq, const void* xk, const void* dyq, const void* dyk,
+                             const void* gain_q, const void* gain_k, void* dxq, void* dxk,
+                             float* dparams, int64_t rows, int32_t Dh, int32_t dtype, float eps,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = qk_norm_check(rows, Dh, dtype, eps);
+  if (rc != DA_OK || rows == 0) return rc;
+  const void* ptrs[8] = {xq, xk, dyq, dyk, gain_q, gain_k, dxq, dxk};
+  for (const void* p : ptrs) {
+    if (!p) return DA_ERR_NULL;
+    if (((uintptr_t)p & 15) != 0) return DA_ERR_ALIGN;
+  }
+  if (!dparams) return DA_ERR_NULL;
+  if (((uintptr_t)dparams & 3) != 0) return DA_ERR_ALIGN;
+  size_t need = 0;
+  dilated_attn_qk_norm_workspace_bytes(rows, &need);
+  if (!workspace || workspace_bytes < need) return DA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255) != 0) return DA_ERR_ALIGN;
+  const size_t tb = (size_t)rows * kDh * (dtype == DA_BF16 ? 2 : 4);
+  const size_t pb = (size_t)kDh * (dtype == DA_BF16 ? 2 : 4);
+  const size_t db = 4 * kDh * sizeof(float);
+  const void* ins[6] = {xq, xk, dyq, dyk, gain_q, gain_k};
+  const size_t isz[6] = {tb, tb, tb, tb, pb, pb};
+  const void* outs[4] = {dxq, dxk, dparams, workspace};
+  const size_t osz[4] = {tb, tb, db, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], osz[i], ins[j], isz[j])) return DA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], osz[i], outs[j], osz[j])) return DA_ERR_ALIAS;
+  }
+  da::QkNormArgs a;
+  memset(&a, 0, sizeof a);
+  a.xq = xq;
+  a.xk = xk;
+  a.dyq = dyq;
+  a.dyk = dyk;
+  a.dxq = dxq;
+  a.dxk = dxk;
+  a.gq = gain_q;
+  a.gk = gain_k;
+  a.partials = reinterpret_cast<float*>(workspace);
+  a.dparams = dparams;
+  a.rows = rows;
+  a.eps = eps;
+  const hipError_t e =
+      da::launch_qk_norm_bwd(a, dtype == DA_BF16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
 int dilated_attn_gather_map(int64_t N, int32_t H, da_pattern pattern, int32_t h, int64_t* dev_out,

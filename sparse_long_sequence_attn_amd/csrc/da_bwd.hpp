@@ -52,4 +52,24 @@ struct BwdRowArgs {
   PatDev pat[kMaxPat];  // caller's order
 };
 
+// qk_norm over rows of kDh values, both tensors in one launch.
+struct QkNormArgs {
+  const void* xq;
+  const void* xk;
+  void* yq;        // forward outputs
+  void* yk;
+  const void* dyq;  // backward inputs
+  const void* dyk;
+  void* dxq;       // backward outputs
+  void* dxk;
+  const void* gq;  // gains and biases, kDh values each
+  const void* bq;
+  const void* gk;
+  const void* bk;
+  float* partials;  // backward: [2][blocks][2 * kDh]
+  float* dparams;   // backward: [2 (q, k)][2 (gain, bias)][kDh]
+  int64_t rows;
+  float eps;
+};
+
 }  // namespace da

@@ -29,6 +29,13 @@ hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, int nw, bool causal, int64_
                         hipStream_t st);
 hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st);
 
+// qk_norm (qknorm_kernel.hip): blocks per tensor for `rows` rows; forward;
+// backward (row gradients, per-block partials of the gain and bias
+// gradients, then their fixed-order sum).
+int64_t qk_norm_blocks(int64_t rows);
+hipError_t launch_qk_norm_fwd(const QkNormArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_qk_norm_bwd(const QkNormArgs& a, bool bf16, hipStream_t st);
+
 // Test hooks: dump the gather map / the inverse (coverage) map of one
 // pattern for one head, computed with the kernels' own index functions.
 hipError_t launch_gather_map(const PatDev& p, int32_t h, int64_t* out, hipStream_t st);

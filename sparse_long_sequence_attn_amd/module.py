@@ -9,14 +9,16 @@ follow the plainest reading of the pages: queries, keys and values are
 linear maps of x (LONGNET blog, "About the Transformer model" and "Token
 expansion reaches 1 billion+"), qk_norm layer-normalises each head's query
 and key vectors, the dilated attention runs in this library's kernels, and
-an output projection maps the heads back to dim. The projections and the
-layer norms are plain library operations (torch's GEMMs and LayerNorm).
+an output projection maps the heads back to dim. The projections are plain
+library GEMMs (torch), with the weight gradients split over the long row
+dimension so that they fill the chip; qk_norm runs in this library's fused
+layer-norm kernels (both tensors in one launch each way).
 """
 from typing import Optional, Sequence, Tuple, Union
 
 import torch
 
-from . import BwdProblem, Problem
+from . import BwdProblem, Problem, qk_norm_bwd, qk_norm_fwd
 
 Pattern = Tuple[int, int]
 
@@ -41,6 +43,75 @@ class DilatedAttnFunction(torch.autograd.Function):
         return dq, dk, dv, None, None, None
 
 
+class QKNormFunction(torch.autograd.Function):
+    """(yq, yk) = layer norm of every 64-value row of xq and xk."""
+
+    @staticmethod
+    def forward(ctx, xq, xk, gq, bq, gk, bk, eps):
+        xq, xk = xq.contiguous(), xk.contiguous()
+        yq, yk = qk_norm_fwd(xq, xk, gq, bq, gk, bk, eps)
+        ctx.save_for_backward(xq, xk, gq, gk)
+        ctx.eps = eps
+        return yq, yk
+
+    @staticmethod
+    def backward(ctx, dyq, dyk):
+        xq, xk, gq, gk = ctx.saved_tensors
+        dxq, dxk, dp = qk_norm_bwd(xq, xk, dyq.contiguous(), dyk.contiguous(), gq, gk, ctx.eps)
+        dp = dp.to(gq.dtype)
+        return dxq, dxk, dp[0, 0], dp[0, 1], dp[1, 0], dp[1, 1], None
+
+
+def _weight_grad(dy2, x2):
+    """dW = dy2^T x2 for [R, out] and [R, in] row-major operands. A single
+    GEMM over R = B * N rows leaves most of the chip idle (a 512 x 512 output
+    is only a few dozen tiles), so long R is split into 32 chunks, one
+    batched GEMM computes the chunk products (left operand a transposed view,
+    right operand contiguous) and their float32 sum is rounded once."""
+    R = dy2.shape[0]
+    S = 32
+    if R % S == 0 and R // S >= 2048:
+        part = torch.bmm(dy2.view(S, R // S, -1).transpose(1, 2), x2.view(S, R // S, -1))
+        acc = torch.float32 if dy2.dtype in (torch.bfloat16, torch.float16) else dy2.dtype
+        return part.sum(0, dtype=acc).to(dy2.dtype)
+    return torch.mm(dy2.t(), x2)
+
+
+class ProjectionFunction(torch.autograd.Function):
+    """(y_1 .. y_n) = (x W_1^T + b_1, ..., x W_n^T + b_n) for one input x
+    [R, in]; the backward accumulates dx over the n products in place."""
+
+    @staticmethod
+    def forward(ctx, x2, n, *wb):
+        ws, bs = wb[:n], wb[n:]
+        ctx.save_for_backward(x2, *ws)
+        ctx.n, ctx.has_bias = n, [b is not None for b in bs]
+        return tuple(torch.nn.functional.linear(x2, w, b) for w, b in zip(ws, bs))
+
+    @staticmethod
+    def backward(ctx, *dys):
+        x2, *ws = ctx.saved_tensors
+        dx = None
+        dws, dbs = [], []
+        for dy, w, hb in zip(dys, ws, ctx.has_bias):
+            dy = dy.contiguous()
+            dx = torch.mm(dy, w) if dx is None else torch.addmm(dx, dy, w)
+            dws.append(_weight_grad(dy, x2))
+            dbs.append(dy.sum(0) if hb else None)
+        return (dx, None, *dws, *dbs)
+
+
+def _project(x, layers):
+    """Apply nn.Linear layers that share the input x [..., in]."""
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    ys = ProjectionFunction.apply(x2, len(layers), *[l.weight for l in layers],
+                                  *[l.bias for l in layers])
+    return [y.view(*lead, y.shape[-1]) for y in ys]
+
+
 def dilated_attention(q, k, v, patterns: Sequence[Pattern], causal: bool = True,
                       scale: Optional[float] = None, return_lse: bool = False):
     """Dilated attention with autograd support. q, k, v: [B, N, H, 64] GPU
@@ -60,9 +131,11 @@ class DilatedAttention(torch.nn.Module):
 
     dilation_rate and segment_size are ints (one pattern, as in the README's
     usage) or equal-length sequences (a mixture of patterns, as in LongNet's
-    experiments). heads * 64 must equal dim. qk_norm adds one LayerNorm over
+    experiments). heads * 64 must equal dim. qk_norm adds one layer norm over
     the 64 values of every head's query and one for keys (gain and bias
-    shared by all heads). bias adds biases to the four projections."""
+    shared by all heads, held by the q_norm / k_norm LayerNorm containers and
+    applied by the library's kernels). bias adds biases to the four
+    projections."""
 
     HEAD_DIM = 64
 
@@ -91,11 +164,9 @@ class DilatedAttention(torch.nn.Module):
     def forward(self, x):
         B, N, _ = x.shape
         shape = (B, N, self.heads, self.HEAD_DIM)
-        q = self.to_q(x).view(shape)
-        k = self.to_k(x).view(shape)
-        v = self.to_v(x).view(shape)
+        q, k, v = (t.view(shape) for t in _project(x, [self.to_q, self.to_k, self.to_v]))
         if self.qk_norm:
-            q = self.q_norm(q)
-            k = self.k_norm(k)
+            q, k = QKNormFunction.apply(q, k, self.q_norm.weight, self.q_norm.bias,
+                                        self.k_norm.weight, self.k_norm.bias, self.q_norm.eps)
         o = dilated_attention(q, k, v, self.patterns, self.causal, self.scale)
-        return self.to_out(o.view(B, N, self.dim))
+        return _project(o.view(B, N, self.dim), [self.to_out])[0]

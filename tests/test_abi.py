@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_native.SIGNATURES)
@@ -230,3 +230,58 @@ def test_bwd_workspace_bytes_errors(lib):
     assert lib.dilated_attn_bwd_workspace_bytes(1, 60, 4, 64, arr, 1, 1, ctypes.byref(out)) == -2
     assert lib.dilated_attn_bwd_workspace_bytes(0, 64, 4, 64, arr, 1, 1, ctypes.byref(out)) == 0
     assert out.value == 0
+
+
+# ---------------------------------------------------------------- qk_norm
+
+XQ, XK, GQ, BQ, GK, BK, YQ, YK = (A * i for i in range(11, 19))
+DPAR, QWS = A * 19, A * 20
+
+
+def qkn_fwd(lib, xq=XQ, xk=XK, gq=GQ, bq=BQ, gk=GK, bk=BK, yq=YQ, yk=YK, rows=256, Dh=64,
+            dtype=_native.DA_BF16, eps=1e-5):
+    return lib.dilated_attn_qk_norm_fwd(xq, xk, gq, bq, gk, bk, yq, yk, rows, Dh, dtype, eps, None)
+
+
+def qkn_bwd(lib, xq=XQ, xk=XK, dyq=YQ, dyk=YK, gq=GQ, gk=GK, dxq=DQ, dxk=DK, dpar=DPAR, rows=256,
+            Dh=64, dtype=_native.DA_BF16, eps=1e-5, ws=QWS, wsb=1 << 20):
+    return lib.dilated_attn_qk_norm_bwd(xq, xk, dyq, dyk, gq, gk, dxq, dxk, dpar, rows, Dh, dtype,
+                                        eps, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(xq=None), -1), (dict(bk=None), -1), (dict(yk=None), -1),
+    (dict(rows=-1), -2), (dict(dtype=3), -4), (dict(Dh=32), -5),
+    (dict(xq=XQ + 8), -7), (dict(gk=GK + 4), -7), (dict(yq=YQ + 2), -7),
+    (dict(yq=XQ), -8), (dict(yk=XK + 64), -8), (dict(yk=YQ), -8), (dict(yq=GQ), -8),
+    (dict(eps=0.0), -9), (dict(eps=-1.0), -9), (dict(eps=math.nan), -9),
+])
+def test_qk_norm_fwd_invalid_calls_rejected(lib, kwargs, code):
+    assert qkn_fwd(lib, **kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dyq=None), -1), (dict(dpar=None), -1), (dict(dxk=None), -1),
+    (dict(rows=-5), -2), (dict(dtype=2), -4), (dict(Dh=128), -5),
+    (dict(ws=None), -6), (dict(wsb=16), -6),
+    (dict(dxq=DQ + 8), -7), (dict(dpar=DPAR + 2), -7), (dict(ws=QWS + 16), -7),
+    (dict(dxq=XQ), -8), (dict(dxk=YK), -8), (dict(dpar=GK), -8), (dict(ws=DQ), -8),
+    (dict(dxk=DQ), -8),
+    (dict(eps=math.inf), -9),
+])
+def test_qk_norm_bwd_invalid_calls_rejected(lib, kwargs, code):
+    assert qkn_bwd(lib, **kwargs) == code
+
+
+def test_qk_norm_zero_rows_is_a_no_op(lib):
+    assert qkn_fwd(lib, rows=0, xq=None, xk=None, yq=None, yk=None) == 0
+    assert qkn_bwd(lib, rows=0, xq=None, dxq=None, ws=None, wsb=0) == 0
+
+
+def test_qk_norm_workspace_bytes(lib):
+    assert _native.qk_norm_workspace_bytes(0) == 0
+    assert _native.qk_norm_workspace_bytes(1) == 2 * 1 * 128 * 4
+    assert _native.qk_norm_workspace_bytes(32 * 1024 * 100) == 2 * 1024 * 128 * 4
+    out = ctypes.c_size_t(0)
+    assert lib.dilated_attn_qk_norm_workspace_bytes(-1, ctypes.byref(out)) == -2
+    assert lib.dilated_attn_qk_norm_workspace_bytes(5, None) == -1
