@@ -121,8 +121,11 @@ struct Smem {
 
 // NW waves per workgroup, each owning QB blocks of 32 query rows (so every
 // K and V fragment read from LDS feeds QB MFMAs); BN keys per LDS tile.
+// 4 waves per SIMD: the bf16 4-wave configuration fits in 128 VGPRs without
+// spills (configurations that do not fit keep their natural allocation).
 template <int NW, int QB, int BN, bool CAUSAL, bool FINAL, bool BF>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+attn_fwd_kernel(const AttnArgs a) {
   using T = typename std::conditional<BF, __bf16, float>::type;
   using SM = Smem<BF, BN>;
   constexpr int QW = 32 * QB;  // query rows per wave
@@ -269,15 +272,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     // key blocks (32 keys) of this tile that some query of the wave sees;
     // later blocks are skipped (their scores stay -inf, their PV is skipped)
     const int32_t kend = CAUSAL ? qw0 + QW : L;
-    const int nkb = min(KB, (kend - kt * BN + 31) / 32);
+    // wave-uniform (kept in a scalar register so the block branches are scalar)
+    const int nkb = __builtin_amdgcn_readfirstlane(min(KB, (kend - kt * BN + 31) / 32));
     f32x16 S[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      if (kb >= nkb) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) S[kb][qb][v] = kb < nkb ? 0.f : -INFINITY;
-      if (kb >= nkb) continue;
+          for (int v = 0; v < 16; ++v) S[kb][qb][v] = -INFINITY;
+        continue;
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) S[kb][qb] = f32x16{};
       const int row = kb * 32 + n;
       if constexpr (BF) {
 #pragma unroll
@@ -310,12 +318,12 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
       if (CAUSAL) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int32_t qs = qw0 + 32 * qb;
+          const int32_t qs = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
           if (kb0 == qs) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
               if (8 * (v >> 2) + (v & 3) > n - 4 * hh) S[kb][qb][v] = -INFINITY;
-          } else if (kb0 > qs) {
+          } else if (QB > 1 && kb0 > qs) {  // with one query block nkb excludes these
 #pragma unroll
             for (int v = 0; v < 16; ++v) S[kb][qb][v] = -INFINITY;
           }
@@ -364,7 +372,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
     }
 
     if constexpr (BF) {
-      bf16x8 pb[QB][2 * KB];
+      // P rounded to bf16 once: the same packed registers feed the PV MFMA
+      // and the row sum
+      u32x4 pw[QB][2 * KB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float lsum = 0.f;
@@ -377,8 +387,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
             bf16x2 pr;
             pr[0] = (__bf16)p0;
             pr[1] = (__bf16)p1;
-            pb[qb][c][e] = pr[0];
-            pb[qb][c][e + 1] = pr[1];
+            pw[qb][c][e >> 1] = __builtin_bit_cast(uint32_t, pr);
             const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
             lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
           }
@@ -406,7 +415,8 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(const AttnArgs a) {
           const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb][c], O[db][qb], 0, 0, 0);
+            O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                vf, __builtin_bit_cast(bf16x8, pw[qb][c]), O[db][qb], 0, 0, 0);
         }
       }
     } else {
