@@ -248,8 +248,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
   const float* lse_row = a.lse + g.bh * a.N;
   const float* d_row = a.dvec + g.bh * a.N;
 
-  const int32_t kw0 = k0 + 32 * wv;  // this wave's first key
-  const int32_t mk = kw0 + n;        // this lane's key
+  // this wave's first key, wave-uniform (scalar branches below)
+  const int32_t kw0 = __builtin_amdgcn_readfirstlane(k0 + 32 * wv);
+  const int32_t mk = kw0 + n;  // this lane's key
   RowFrag<BF> kf, vf;                // B operands of S = Q K^T and dP = dout V^T
   kf.load(rk, (uint32_t)mk * g.mbytes, hh);
   vf.load(rv, (uint32_t)mk * g.mbytes, hh);
@@ -328,21 +329,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
       }
       // register v: query qb*32 + 8(v/4) + 4hh + v%4 of the tile, key n
       float pv[16], sv[16];
-      const bool diag = CAUSAL && qs == kw0;
+      auto probs = [&](bool diag) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int qi = qb * 32 + 8 * gq + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qi);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + qi);
+        for (int gq = 0; gq < 4; ++gq) {
+          const int qi = qb * 32 + 8 * gq + 4 * hh;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qi);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + qi);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int v = 4 * gq + j;
-          float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l4[j]));
-          if (diag && 8 * gq + 4 * hh + j < n) p = 0.f;
-          pv[v] = p;
-          sv[v] = p * (dP[v] - d4[j]);
+          for (int j = 0; j < 4; ++j) {
+            const int v = 4 * gq + j;
+            float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l4[j]));
+            if (diag && 8 * gq + 4 * hh + j < n) p = 0.f;
+            pv[v] = p;
+            sv[v] = p * (dP[v] - d4[j]);
+          }
         }
-      }
+      };
+      if (CAUSAL && qs == kw0)  // the diagonal block: keys after their query masked
+        probs(true);
+      else
+        probs(false);
       if constexpr (BF) {
         const lds_cptr qbase = (lds_cptr)smem + buf * kBufBytes;
         const lds_cptr dbase = qbase + kTileBytes;
@@ -431,8 +437,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, g.range);
   const auto rdo = dev_rsrc(reinterpret_cast<const T*>(a.dout) + rowbase, g.range);
 
-  const int32_t qw0 = q0 + 32 * wv;  // this wave's first query
-  const int32_t mq = qw0 + n;        // this lane's query
+  // this wave's first query, wave-uniform (scalar branches below)
+  const int32_t qw0 = __builtin_amdgcn_readfirstlane(q0 + 32 * wv);
+  const int32_t mq = qw0 + n;  // this lane's query
   RowFrag<BF> qf, df;                // B operands of S^T = K Q^T and dP^T = V dout^T
   qf.load(rq, (uint32_t)mq * g.mbytes, hh);
   df.load(rdo, (uint32_t)mq * g.mbytes, hh);
@@ -498,13 +505,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
       }
       // register v: key kb0 + 8(v/4) + 4hh + v%4, query mq
       float sv[16];
-      const bool diag = CAUSAL && kb0 == qw0;
+      auto probs = [&](bool diag) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l2));
-        if (diag && 8 * (v >> 2) + 4 * hh + (v & 3) > n) p = 0.f;
-        sv[v] = p * (dP[v] - dd);
-      }
+        for (int v = 0; v < 16; ++v) {
+          float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l2));
+          if (diag && 8 * (v >> 2) + 4 * hh + (v & 3) > n) p = 0.f;
+          sv[v] = p * (dP[v] - dd);
+        }
+      };
+      if (CAUSAL && kb0 == qw0)  // the diagonal block: keys after the query masked
+        probs(true);
+      else
+        probs(false);
       if constexpr (BF) {
         const lds_cptr kbase = (lds_cptr)smem + buf * kBufBytes;
 #pragma unroll
