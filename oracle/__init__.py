@@ -46,6 +46,10 @@ def _bind(path):
         bw.argtypes = [P, P, P, P, ctypes.c_int, i64, i64, i32, i32, P, i32, i32,
                        ctypes.c_double, ctypes.c_int, P, P, P]
         bw.restype = ctypes.c_int
+        br = getattr(lib, "orc_bwd_rows_" + sfx)
+        br.argtypes = [P, P, P, P, ctypes.c_int, i64, i64, i32, i32, P, i32, i32,
+                       ctypes.c_double, ctypes.c_int, P, i64, P, P, P]
+        br.restype = ctypes.c_int
     return lib
 
 
@@ -178,6 +182,28 @@ class Oracle:
             raise RuntimeError(f"orc_bwd_{precision} -> {rc}")
         return dq, dk, dv
 
+    def bwd_rows(self, q, k, v, dout, patterns, row_idx, causal=True, scale=None,
+                 want_dq=True, want_dkv=True, precision="f64", threads=0):
+        """Backward pass at selected rows (row formulation). row_idx: int64
+        [n, 3] of (b, t, h). Returns (dq, dk, dv), each [n, Dh] or None."""
+        _check_inputs(q, k, v)
+        _check_inputs(q, dout, dout)
+        lib = self._lib
+        B, N, H, Dh = q.shape
+        row_idx = np.ascontiguousarray(row_idx, dtype=np.int64).reshape(-1, 3)
+        n = row_idx.shape[0]
+        real = np.float64 if precision == "f64" else np.float32
+        fn = lib.orc_bwd_rows_f64 if precision == "f64" else lib.orc_bwd_rows_f32
+        dq = np.empty((n, Dh), dtype=real) if want_dq else None
+        dk = np.empty((n, Dh), dtype=real) if want_dkv else None
+        dv = np.empty((n, Dh), dtype=real) if want_dkv else None
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _in_dtype(q), B, N, H, Dh,
+                _patterns(patterns), len(patterns), 1 if causal else 0, float(scale or 0.0),
+                int(threads), _ptr(row_idx), n, _ptr(dq), _ptr(dk), _ptr(dv))
+        if rc:
+            raise RuntimeError(f"orc_bwd_rows_{precision} -> {rc}")
+        return dq, dk, dv
+
 
 _default = None
 
@@ -211,3 +237,7 @@ def rows(*args, **kwargs):
 
 def bwd(*args, **kwargs):
     return default().bwd(*args, **kwargs)
+
+
+def bwd_rows(*args, **kwargs):
+    return default().bwd_rows(*args, **kwargs)

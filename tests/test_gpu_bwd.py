@@ -144,6 +144,75 @@ def test_bwd_workload_full(torch_cuda, name):
     compare_grads(got, ref, w.dtype, w.patterns, name)
 
 
+# ---------------------------------------------------------------- one GPU's million tokens
+
+def test_bwd_million_token_workload_sampled(torch_cuda):
+    """The million-token workload (six patterns, drawn on the GPU): dq on
+    sampled rows and dk, dv on sampled key rows against the oracle's row
+    formulation, plus identities of the full gradients (the key gradients of
+    a (batch, head) sum to zero; the value gradients sum to the summed dout,
+    every row being gathered; <q, dq> = <k, dk>), with the summation-noise
+    allowance tol * ||summands||_2."""
+    import oracle as orc_mod
+    from sparse_long_sequence_attn_amd.workloads import DOUT_SEED_OFFSET, device_inputs
+    from tests.test_gpu_parity import sample_rows
+
+    torch = torch_cuda
+    w = WORKLOADS["paper_mixture_plus_w65536_n1m_h16_bf16"]
+    qt, kt, vt = device_inputs(w)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + DOUT_SEED_OFFSET)
+    dt = torch.randn(qt.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    fwd = Problem(qt, kt, vt, w.patterns, w.causal)
+    fwd.run()
+    bp = BwdProblem(qt, kt, vt, fwd.out, fwd.lse, dt, w.patterns, w.causal)
+    for t in (bp.dq, bp.dk, bp.dv):
+        t.fill_(float("nan"))
+    bp.run()
+    torch.cuda.synchronize()
+    for t in (bp.dq, bp.dk, bp.dv):
+        assert not torch.isnan(t).any().item()
+
+    from sparse_long_sequence_attn_amd.workloads import from_torch_bits
+    q, k, v, d = (from_torch_bits(x) for x in (qt, kt, vt, dt))
+    rq = sample_rows(w, per_head=48, seed=1)
+    rng = np.random.default_rng(2)
+    rk = []
+    for h in range(w.H):
+        for (pw, r) in w.patterns[:2]:  # last gathered row of a segment: few queries see it
+            off = h % r
+            L = -(-(min(pw, w.N) - off) // r)
+            rk.append((0, off + (L - 1) * r, h))
+        rk.append((0, int(rng.integers(0, w.N)), h))
+    rk = np.array(rk, dtype=np.int64)
+    oq, _, _ = orc_mod.bwd_rows(q, k, v, d, w.patterns, rq, causal=w.causal, want_dkv=False)
+    _, ok, ov = orc_mod.bwd_rows(q, k, v, d, w.patterns, rk, causal=w.causal, want_dq=False)
+
+    def rows_of(t, rr):
+        i = torch.from_numpy(rr).to(t.device)
+        return t[i[:, 0], i[:, 1], i[:, 2]].float().cpu().numpy().astype(np.float64)
+
+    for name, got, ref in (("dq", rows_of(bp.dq, rq), oq), ("dk", rows_of(bp.dk, rk), ok),
+                           ("dv", rows_of(bp.dv, rk), ov)):
+        scale = max(1.0, float(np.abs(ref).max()))
+        err = float(np.abs(got - ref).max()) / scale
+        print(f"1M tokens {name}, {len(ref)} rows: max err / scale = {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], name
+
+    tol = TOL["bf16"]
+    dk64, dv64 = bp.dk.double(), bp.dv.double()
+    sk = dk64.sum(dim=1)
+    nk = dk64.pow(2).sum(dim=1).sqrt()
+    assert bool((sk.abs() <= tol * nk).all()), float((sk.abs() / nk).max())
+    sv = dv64.sum(dim=1) - dt.double().sum(dim=1)
+    nv = dv64.pow(2).sum(dim=1).sqrt()
+    assert bool((sv.abs() <= tol * nv).all()), float((sv.abs() / nv).max())
+    qdq = (qt.double() * bp.dq.double()).sum(dim=(1, 3))
+    kdk = (kt.double() * dk64).sum(dim=(1, 3))
+    nq = (qt.double() * bp.dq.double()).pow(2).sum(dim=(1, 3)).sqrt()
+    assert bool(((qdq - kdk).abs() <= tol * (nq + (kt.double() * dk64).pow(2).sum(dim=(1, 3)).sqrt())).all())
+
+
 # ---------------------------------------------------------------- independent check, API paths
 
 def test_bwd_full_window_equals_torch_autograd(torch_cuda):

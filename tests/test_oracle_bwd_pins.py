@@ -224,6 +224,23 @@ def test_bwd_f32_tracks_f64(orc):
     pin_bwd_f32_tracks_f64(orc)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_rows_match_full_backward(orc, causal):
+    """The row formulation (used where the full backward is too large)
+    against the full backward on every row, including rows no pattern
+    gathers and a pattern listed twice."""
+    q, k, v, do = rand4(2, 48, 5, 16, 19)
+    pats = [(16, 3), (48, 2), (8, 1), (16, 3)]
+    dq, dk, dv = orc.bwd(q, k, v, do, pats, causal=causal)
+    rows = np.array([(b, t, h) for b in range(2) for t in range(48) for h in range(5)])
+    gq, gk, gv = orc.bwd_rows(q, k, v, do, pats, rows, causal=causal)
+    idx = (rows[:, 0], rows[:, 1], rows[:, 2])
+    for g, r in ((gq, dq), (gk, dk), (gv, dv)):
+        assert np.abs(g - r[idx]).max() < 1e-12
+    only_q = orc.bwd_rows(q, k, v, do, pats, rows[:7], causal=causal, want_dkv=False)
+    assert only_q[1] is None and np.array_equal(only_q[0], gq[:7])
+
+
 def test_bwd_empty_batch(orc):
     q = np.zeros((0, 16, 2, 8))
     dq, dk, dv = orc.bwd(q, q, q, q, [(8, 2)])
