@@ -109,14 +109,14 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool BF, int BN>
+template <bool BF, int BN, int NBUF = 2>
 struct Smem {
   // bf16: K [BN][64] swizzled, V [BN][72] (144-byte rows); fp32: K [BN][65], V [BN][64]
   static constexpr int kVStride = BF ? kDh + 8 : kDh;
   static constexpr int kKElems = BF ? BN * kDh : BN * (kDh + 1);
   static constexpr int kVElems = BN * kVStride;
   static constexpr int kElemBytes = BF ? 2 : 4;
-  static constexpr int kBytes = 2 * (kKElems + kVElems) * kElemBytes;
+  static constexpr int kBytes = NBUF * (kKElems + kVElems) * kElemBytes;
 };
 
 // NW waves per workgroup, each owning QB blocks of 32 query rows (so every
@@ -127,16 +127,26 @@ template <int NW, int QB, int BN, bool CAUSAL, bool FINAL, bool BF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 attn_fwd_kernel(const AttnArgs a) {
   using T = typename std::conditional<BF, __bf16, float>::type;
-  using SM = Smem<BF, BN>;
+  // one-wave workgroups serve segments of at most 32 gathered rows (one key
+  // tile): a single LDS buffer, so more workgroups fit on a CU
+  constexpr int NBUF = NW == 1 ? 1 : 2;
+  using SM = Smem<BF, BN, NBUF>;
   constexpr int QW = 32 * QB;  // query rows per wave
   constexpr int BM = QW * NW;  // query rows per workgroup
   constexpr int NT = 64 * NW;
   constexpr int KB = BN / 32;
   static_assert(BN % 32 == 0 && BN <= 128, "key tile");
 
-  __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
+  // epilogue staging of one-wave workgroups: 32 normalised rows (fp32,
+  // 68-float stride for conflict-free 16-byte writes) and per-row position,
+  // kind and lse
+  constexpr int kStageStride = kDh + 4;
+  constexpr int kStageBytes = 32 * kStageStride * 4 + 32 * 12;
+  constexpr int kSmemBytes =
+      NW == 1 && NW * kStageBytes > SM::kBytes ? NW * kStageBytes : SM::kBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   T* const Ks = reinterpret_cast<T*>(smem);
-  T* const Vs = Ks + 2 * SM::kKElems;
+  T* const Vs = Ks + NBUF * SM::kKElems;  // the K buffers, then the V buffers
 
   Tile tl;
   if (!decode_tile(a, blockIdx.x, &tl)) return;
@@ -401,7 +411,7 @@ attn_fwd_kernel(const AttnArgs a) {
       // the transpose read then hands lane i the four keys of dim i.
       const char __attribute__((address_space(3)))* vbase =
           (const char __attribute__((address_space(3)))*)smem +
-          (2 * SM::kKElems + buf * SM::kVElems) * sizeof(T);
+          (NBUF * SM::kKElems + buf * SM::kVElems) * sizeof(T);
       const uint32_t vlane = (uint32_t)((4 * (g16 >> 1) + (m16 >> 2)) * SM::kVStride +
                                         16 * (g16 & 1) + 4 * (m16 & 3)) * 2;
 #pragma unroll
@@ -452,77 +462,65 @@ attn_fwd_kernel(const AttnArgs a) {
   load_tile(0);
   store_tile(0);
   __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load_tile(kt + 1);
-    if (kt < nkt_w) compute(buf, kt);
-    if (kt + 1 < nkt) store_tile(buf ^ 1);
-    __syncthreads();
+  if constexpr (NBUF == 2) {
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nkt) load_tile(kt + 1);
+      if (kt < nkt_w) compute(buf, kt);
+      if (kt + 1 < nkt) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) {
+      if (kt > 0) {
+        __syncthreads();  // the previous tile is consumed before it is overwritten
+        load_tile(kt);
+        store_tile(0);
+        __syncthreads();
+      }
+      if (kt < nkt_w) compute(0, kt);
+    }
   }
 
-  // ---- epilogue: normalise and write each valid query row
+  // ---- epilogue: normalise every valid query row and write it
   float l_tot[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) l_tot[qb] = pair_sum(l_run[qb]);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    if (mq[qb] >= L) continue;
-    const float inv = __builtin_amdgcn_rcpf(l_tot[qb]);
-    const float lse2 = m_run[qb] + __log2f(l_tot[qb]);
-    const int64_t pos = gathered_pos(tl.seg, wp, off, r, mq[qb]);
-    // A row that no other pattern gathers is final here and is written to
-    // out / lse directly; rows several patterns gather go through the
-    // partial buffers and the merge kernel.
-    bool direct = FINAL;
-    if constexpr (!FINAL) {
-      int cover = 0;
-      for (int i = 0; i < a.np; ++i)
-        cover += compact_index((uint32_t)pos, a.pat[i], head_offset(tl.h, a.pat[i].r)) >= 0;
-      direct = cover == 1;
-    }
-    if (direct) {
-      T* orow = reinterpret_cast<T*>(a.out) + headbase;
-      float* lse_row = a.lse + ((int64_t)tl.b * a.H + tl.h) * a.N;
-      auto put = [&](int64_t t, bool zero) {
-        T* dst = orow + t * rs + 4 * hh;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d = db * 32 + 8 * g;
-            if constexpr (BF) {
-              bf16x2 x0, x1;
-              x0[0] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 0] * inv);
-              x0[1] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 1] * inv);
-              x1[0] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 2] * inv);
-              x1[1] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 3] * inv);
-              *reinterpret_cast<u32x2*>(dst + d) =
-                  u32x2{__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1)};
-            } else {
-              f32x4 x;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) x[e] = zero ? 0.f : O[db][qb][4 * g + e] * inv;
-              *reinterpret_cast<f32x4*>(dst + d) = x;
-            }
-          }
-        if (hh == 0) lse_row[t] = zero ? -INFINITY : lse2 * kLn2;
-      };
-      put(pos, false);
-      if constexpr (FINAL) {
-        // one pattern: positions of this segment that the head does not
-        // gather (the r-1 after each gathered row and, before the first
-        // one, the offset rows) get 0 and -inf here
-        const int64_t seg_end = seg0 + wp;
-        for (int j = 1; j < r; ++j) {
-          if (pos + j >= seg_end) break;
-          put(pos + j, true);
-        }
-        if (mq[qb] == 0)
-          for (int j = 0; j < off; ++j) put(seg0 + j, true);
+  T* const orow = reinterpret_cast<T*>(a.out) + headbase;
+  float* const lse_row = a.lse + ((int64_t)tl.b * a.H + tl.h) * a.N;
+  const int64_t seg_end = seg0 + wp;
+
+  if constexpr (NW == 1) {
+    // Segments of at most 32 rows are bound by their writes: the rows go out
+    // row-contiguous. Each wave stages its 32 rows (fp32) and their metadata
+    // in its own LDS region (the K/V tile is no longer read), then 16 lanes
+    // write each row: 128 contiguous bytes of bf16 output (256 of fp32 output
+    // or of an fp32 partial), where the MFMA layout would scatter 8-byte
+    // pieces of 32 rows per store.
+    float* const srow = reinterpret_cast<float*>(smem + wv * kStageBytes);
+    int32_t* const mpos = reinterpret_cast<int32_t*>(srow + 32 * kStageStride);
+    int32_t* const mkind = mpos + 32;  // 0: no row, 1: final output, 2: partial
+    float* const mlse = reinterpret_cast<float*>(mkind + 32);
+    const int sr = lane >> 4;  // row within a pass of 4 rows
+    const int sc = lane & 15;  // 4-value chunk of the row
+    auto store4 = [&](T* dst, const f32x4& x) {
+      if constexpr (BF) {
+        bf16x2 x0, x1;
+        x0[0] = (__bf16)x[0];
+        x0[1] = (__bf16)x[1];
+        x1[0] = (__bf16)x[2];
+        x1[1] = (__bf16)x[3];
+        *reinterpret_cast<u32x2*>(dst) =
+            u32x2{__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1)};
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = x;
       }
-    } else {
-      const int64_t prow = (((int64_t)tl.b * a.H + tl.h) * P.nseg + tl.seg) * P.lmax + mq[qb];
-      float* po = a.ws + P.po_off + prow * kDh + 4 * hh;
+    };
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      __syncthreads();  // LDS free: tile (or the previous query block's rows) consumed
+      const bool valid = mq[qb] < L;
+      const float inv = valid ? __builtin_amdgcn_rcpf(l_tot[qb]) : 0.f;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -530,9 +528,132 @@ attn_fwd_kernel(const AttnArgs a) {
           f32x4 x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = O[db][qb][4 * g + e] * inv;
-          *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g) = x;
+          *reinterpret_cast<f32x4*>(srow + n * kStageStride + db * 32 + 8 * g + 4 * hh) = x;
         }
-      if (hh == 0) a.ws[P.pl_off + prow] = lse2;
+      if (hh == 0) {
+        int32_t kind = 0, pos32 = -1;
+        if (valid) {
+          const int64_t pos = gathered_pos(tl.seg, wp, off, r, mq[qb]);
+          pos32 = (int32_t)pos;  // positions are below 2^31
+          // a row no other pattern gathers is final here; rows several
+          // patterns gather go through the partial buffers and the merge
+          kind = 1;
+          if constexpr (!FINAL) {
+            int cover = 0;
+            for (int i = 0; i < a.np; ++i)
+              cover += compact_index((uint32_t)pos, a.pat[i], head_offset(tl.h, a.pat[i].r)) >= 0;
+            kind = cover == 1 ? 1 : 2;
+          }
+        }
+        mpos[n] = pos32;
+        mkind[n] = kind;
+        mlse[n] = m_run[qb] + __log2f(l_tot[qb]);
+      }
+      __syncthreads();
+      const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int R = 4 * i + sr;
+        const int32_t kind = mkind[R];
+        if (kind == 0) continue;
+        const int64_t pos = mpos[R];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(srow + R * kStageStride + 4 * sc);
+        const float lse2 = mlse[R];
+        const int32_t m = qw0 + 32 * qb + R;  // gathered index of the row
+        if (kind == 1) {
+          store4(orow + pos * rs + 4 * sc, x);
+          if (sc == 0) lse_row[pos] = lse2 * kLn2;
+          if constexpr (FINAL) {
+            // one pattern: positions of this segment that the head does not
+            // gather (the r-1 after each gathered row and, before the first
+            // one, the offset rows) get 0 and -inf here
+            for (int j = 1; j < r; ++j) {
+              if (pos + j >= seg_end) break;
+              store4(orow + (pos + j) * rs + 4 * sc, zero4);
+              if (sc == 0) lse_row[pos + j] = -INFINITY;
+            }
+            if (m == 0)
+              for (int j = 0; j < off; ++j) {
+                store4(orow + (seg0 + j) * rs + 4 * sc, zero4);
+                if (sc == 0) lse_row[seg0 + j] = -INFINITY;
+              }
+          }
+        } else {
+          const int64_t prow = (((int64_t)tl.b * a.H + tl.h) * P.nseg + tl.seg) * P.lmax + m;
+          *reinterpret_cast<f32x4*>(a.ws + P.po_off + prow * kDh + 4 * sc) = x;
+          if (sc == 0) a.ws[P.pl_off + prow] = lse2;
+        }
+      }
+    }
+  } else {
+    // Long segments are bound by the softmax: rows are written straight from
+    // the MFMA layout.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (mq[qb] >= L) continue;
+      const float inv = __builtin_amdgcn_rcpf(l_tot[qb]);
+      const float lse2 = m_run[qb] + __log2f(l_tot[qb]);
+      const int64_t pos = gathered_pos(tl.seg, wp, off, r, mq[qb]);
+      // A row that no other pattern gathers is final here and is written to
+      // out / lse directly; rows several patterns gather go through the
+      // partial buffers and the merge kernel.
+      bool direct = FINAL;
+      if constexpr (!FINAL) {
+        int cover = 0;
+        for (int i = 0; i < a.np; ++i)
+          cover += compact_index((uint32_t)pos, a.pat[i], head_offset(tl.h, a.pat[i].r)) >= 0;
+        direct = cover == 1;
+      }
+      if (direct) {
+        auto put = [&](int64_t t, bool zero) {
+          T* dst = orow + t * rs + 4 * hh;
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int d = db * 32 + 8 * g;
+              if constexpr (BF) {
+                bf16x2 x0, x1;
+                x0[0] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 0] * inv);
+                x0[1] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 1] * inv);
+                x1[0] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 2] * inv);
+                x1[1] = (__bf16)(zero ? 0.f : O[db][qb][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(dst + d) =
+                    u32x2{__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1)};
+              } else {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = zero ? 0.f : O[db][qb][4 * g + e] * inv;
+                *reinterpret_cast<f32x4*>(dst + d) = x;
+              }
+            }
+          if (hh == 0) lse_row[t] = zero ? -INFINITY : lse2 * kLn2;
+        };
+        put(pos, false);
+        if constexpr (FINAL) {
+          // one pattern: positions of this segment that the head does not
+          // gather get 0 and -inf here
+          for (int j = 1; j < r; ++j) {
+            if (pos + j >= seg_end) break;
+            put(pos + j, true);
+          }
+          if (mq[qb] == 0)
+            for (int j = 0; j < off; ++j) put(seg0 + j, true);
+        }
+      } else {
+        const int64_t prow = (((int64_t)tl.b * a.H + tl.h) * P.nseg + tl.seg) * P.lmax + mq[qb];
+        float* po = a.ws + P.po_off + prow * kDh + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = O[db][qb][4 * g + e] * inv;
+            *reinterpret_cast<f32x4*>(po + db * 32 + 8 * g) = x;
+          }
+        if (hh == 0) a.ws[P.pl_off + prow] = lse2;
+      }
     }
   }
 }
