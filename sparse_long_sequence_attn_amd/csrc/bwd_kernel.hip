@@ -214,6 +214,51 @@ __device__ inline void put_partial(float* dst, const f32x16 (&acc)[2], float mul
     }
 }
 
+// Row-contiguous writes for one-wave workgroups (segments of at most 32
+// rows, where the kernels are bound by their writes): each lane stages its
+// half row (MFMA layout) in LDS, then 16 lanes write each of the wave's 32
+// rows as one contiguous line - 128 bytes of bf16 (256 of fp32) - instead of
+// 8-byte pieces of 32 rows per store.
+constexpr int kStageStride = kDh + 4;  // floats; conflict-free 16-byte writes
+constexpr int kStageBytes = 32 * kStageStride * 4 + 32 * 8;
+
+__device__ inline void stage_row(float* srow, const f32x16 (&acc)[2], float mul, int n, int hh) {
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * mul;
+      *reinterpret_cast<f32x4*>(srow + n * kStageStride + db * 32 + 8 * g + 4 * hh) = x;
+    }
+}
+
+// Rows of kind 1 go to final + pos * rs, rows of kind 2 to partial + R * kDh
+// (the wave's first gathered row at partial); kind 0 rows are skipped.
+template <bool BF>
+__device__ inline void write_rows(const float* srow, const int32_t* mpos, const int32_t* mkind,
+                                  void* final_base, int64_t rs, float* partial, int lane) {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  const int sr = lane >> 4, sc = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int R = 4 * i + sr;
+    const int32_t kind = mkind[R];
+    if (kind == 0) continue;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(srow + R * kStageStride + 4 * sc);
+    if (kind == 1) {
+      T* dst = reinterpret_cast<T*>(final_base) + (int64_t)mpos[R] * rs + 4 * sc;
+      if constexpr (BF)
+        *reinterpret_cast<u32x2*>(dst) = u32x2{dev_pack_bf16(x[0], x[1]), dev_pack_bf16(x[2], x[3])};
+      else
+        *reinterpret_cast<f32x4*>(dst) = x;
+    } else {
+      *reinterpret_cast<f32x4*>(partial + (int64_t)R * kDh + 4 * sc) = x;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dK, dV
 
 template <int NW, bool CAUSAL, bool BF>
@@ -227,6 +272,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int kTileBytes = kTileElems * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dout, lse2, D
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
+  static_assert(NW != 1 || 2 * kBufBytes >= kStageBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
 
   UnitTile tl;
@@ -391,18 +437,45 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
     __syncthreads();
   }
 
-  if (mk >= g.L) return;
-  const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
-  if (coverage(a, (uint32_t)pos, tl.h) == 1) {
-    const int64_t e = g.headbase + pos * g.rs;
-    put_row<BF>(a.dk, e, dK, a.scale, hh);
-    put_row<BF>(a.dv, e, dV, 1.f, hh);
+  const PatDev& P = a.pat[tl.p];
+  const int64_t slots = P.units * P.lmax;
+  const int64_t prow0 = (g.bh * P.nseg + tl.seg) * P.lmax;  // the unit's first slot
+  if constexpr (NW == 1) {
+    // the tiles are consumed (the loop ended with a barrier); one tensor at
+    // a time through the staging area
+    float* const srow = reinterpret_cast<float*>(smem);
+    int32_t* const mpos = reinterpret_cast<int32_t*>(srow + 32 * kStageStride);
+    int32_t* const mkind = mpos + 32;
+    if (hh == 0) {
+      int32_t kind = 0, pos32 = -1;
+      if (mk < g.L) {
+        const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
+        pos32 = (int32_t)pos;  // positions are below 2^31
+        kind = coverage(a, (uint32_t)pos, tl.h) == 1 ? 1 : 2;
+      }
+      mpos[n] = pos32;
+      mkind[n] = kind;
+    }
+    stage_row(srow, dK, a.scale, n, hh);
+    __syncthreads();
+    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs,
+                   a.ws + P.po_off + (slots + prow0 + kw0) * kDh, lane);
+    __syncthreads();
+    stage_row(srow, dV, 1.f, n, hh);
+    __syncthreads();
+    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dv) + g.headbase, g.rs,
+                   a.ws + P.po_off + (2 * slots + prow0 + kw0) * kDh, lane);
   } else {
-    const PatDev& P = a.pat[tl.p];
-    const int64_t slots = P.units * P.lmax;
-    const int64_t prow = (g.bh * P.nseg + tl.seg) * P.lmax + mk;
-    put_partial(a.ws + P.po_off + (slots + prow) * kDh, dK, a.scale, hh);
-    put_partial(a.ws + P.po_off + (2 * slots + prow) * kDh, dV, 1.f, hh);
+    if (mk >= g.L) return;
+    const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
+    if (coverage(a, (uint32_t)pos, tl.h) == 1) {
+      const int64_t e = g.headbase + pos * g.rs;
+      put_row<BF>(a.dk, e, dK, a.scale, hh);
+      put_row<BF>(a.dv, e, dV, 1.f, hh);
+    } else {
+      put_partial(a.ws + P.po_off + (slots + prow0 + mk) * kDh, dK, a.scale, hh);
+      put_partial(a.ws + P.po_off + (2 * slots + prow0 + mk) * kDh, dV, 1.f, hh);
+    }
   }
 }
 
@@ -418,6 +491,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   constexpr int kTileBytes = BK * ST * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes;  // K, V
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
+  static_assert(NW != 1 || 2 * kBufBytes >= kStageBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
 
   UnitTile tl;
@@ -553,13 +627,29 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
     __syncthreads();
   }
 
-  if (mq >= g.L) return;
-  if (coverage(a, (uint32_t)pos, tl.h) == 1) {
-    put_row<BF>(a.dq, g.headbase + pos * g.rs, dQ, a.scale, hh);
+  const PatDev& P = a.pat[tl.p];
+  const int64_t prow0 = (g.bh * P.nseg + tl.seg) * P.lmax;  // the unit's first slot
+  if constexpr (NW == 1) {
+    float* const srow = reinterpret_cast<float*>(smem);
+    int32_t* const mpos = reinterpret_cast<int32_t*>(srow + 32 * kStageStride);
+    int32_t* const mkind = mpos + 32;
+    if (hh == 0) {
+      int32_t kind = 0;
+      if (mq < g.L) kind = coverage(a, (uint32_t)pos, tl.h) == 1 ? 1 : 2;
+      mpos[n] = mq < g.L ? (int32_t)pos : -1;  // positions are below 2^31
+      mkind[n] = kind;
+    }
+    stage_row(srow, dQ, a.scale, n, hh);
+    __syncthreads();
+    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs,
+                   a.ws + P.po_off + (prow0 + qw0) * kDh, lane);
   } else {
-    const PatDev& P = a.pat[tl.p];
-    const int64_t prow = (g.bh * P.nseg + tl.seg) * P.lmax + mq;
-    put_partial(a.ws + P.po_off + prow * kDh, dQ, a.scale, hh);
+    if (mq >= g.L) return;
+    if (coverage(a, (uint32_t)pos, tl.h) == 1) {
+      put_row<BF>(a.dq, g.headbase + pos * g.rs, dQ, a.scale, hh);
+    } else {
+      put_partial(a.ws + P.po_off + (prow0 + mq) * kDh, dQ, a.scale, hh);
+    }
   }
 }
 
