@@ -175,7 +175,8 @@ def run_bwd(args, w, dev, q, k, v):
         gbs = c.kv_bytes / (kms["kv"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": measured_traffic("bwd", w.name), "kernel": "bwd_kv_kernel",
+    roof.update({"traffic": measured_traffic("bwd", w.name),
+                 "kernel": "bwd_short_kernel" if c.fused else "bwd_kv_kernel",
                  "kernel_ms": round(kms["kv"], 4)})
     result = {
         "metric": METRIC_BWD,
@@ -197,14 +198,15 @@ def run_bwd(args, w, dev, q, k, v):
         "detail": {
             "kernel_ms": {n: round(x, 4) for n, x in kms.items()},
             "tflops_kv_kernel": round(kv_tflops, 2),
-            "tflops_q_kernel": round(q_tflops, 2),
-            "pct_bf16_peak_q_kernel": round(100 * q_tflops / peak, 2),
+            "tflops_q_kernel": None if c.fused else round(q_tflops, 2),
+            "pct_bf16_peak_q_kernel": None if c.fused else round(100 * q_tflops / peak, 2),
             "tflops_algorithmic_step": round(step_tflops, 2),
             "pct_bf16_peak_algorithmic_step": round(100 * step_tflops / peak, 2),
             "flops_algorithmic": c.flops_alg,
             "flops_kv_kernel": c.flops_kv,
             "flops_q_kernel": c.flops_q,
-            "gbs_prep": round(c.prep_bytes / (kms["prep"] / 1e3) / 1e9, 1),
+            "gbs_prep": None if c.fused else round(c.prep_bytes / (kms["prep"] / 1e3) / 1e9, 1),
+            "fused_short_segments": c.fused,
             "gbs_merge": round(c.merge_bytes / (kms["merge"] / 1e3) / 1e9, 1)
             if c.merge_bytes > 0 else None,
             "kv_algorithmic_bytes": c.kv_bytes,

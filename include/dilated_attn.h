@@ -170,6 +170,10 @@ int dilated_attn_bwd(const void* q, const void* k, const void* v, const void* ou
  *  DA_BWD_Q:     the same for dq (needs D);
  *  DA_BWD_MERGE: sums the partials of rows several patterns gather and
  *                writes zeros to rows no pattern gathers.
+ * When every pattern's segments gather at most 32 rows (ceil(min(w, N) / r)
+ * <= 32 for all patterns), DA_BWD_KV runs one kernel that forms D itself and
+ * writes dq, dk and dv (or their partials); DA_BWD_PREP and DA_BWD_Q then
+ * launch nothing.
  * stages is a non-empty OR of these flags (else DA_ERR_ARG); the other
  * arguments and checks are those of dilated_attn_bwd. */
 enum { DA_BWD_PREP = 1, DA_BWD_KV = 2, DA_BWD_Q = 4, DA_BWD_MERGE = 8, DA_BWD_ALL = 15 };

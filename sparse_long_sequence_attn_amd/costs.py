@@ -102,15 +102,21 @@ def cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causal: b
 
 @dataclass
 class BwdCost:
+    """Per-stage work of one backward call. With fused set (every segment
+    gathers at most 32 rows) the KV stage is the one-wave kernel that
+    computes D and all three gradients, and the PREP and Q stages are empty."""
     pairs: float            # useful (query, key) pairs, summed over patterns
     flops_alg: float        # five products per pair (S recomputed, dP, dV, dK, dQ): 10 Dh
-    flops_kv: float         # the dK/dV kernel's products (S, dP, dV, dK): 8 Dh per pair
-    flops_q: float          # the dQ kernel's products (S, dP, dQ): 6 Dh per pair
-    exps: float             # exponentials, once per pair in each of the two kernels
-    prep_bytes: float       # out and dout read, D written
-    kv_bytes: float         # gathered q, k, v, dout rows + lse, D read; dk, dv written
-    q_bytes: float          # gathered q, k, v, dout rows + lse, D read; dq written
+    flops_kv: float         # the KV-stage kernel's products: S, dP, dV, dK (8 Dh per pair),
+                            # fused: all five (10 Dh)
+    flops_q: float          # the dQ kernel's products (S, dP, dQ): 6 Dh per pair; fused: 0
+    exps: float             # exponentials, once per pair in each kernel that forms P
+    prep_bytes: float       # out and dout read, D written; fused: 0
+    kv_bytes: float         # gathered q, k, v, dout rows + lse, D read; dk, dv written;
+                            # fused: q, k, v, dout, out rows + lse read; dq, dk, dv written
+    q_bytes: float          # gathered q, k, v, dout rows + lse, D read; dq written; fused: 0
     merge_bytes: float      # partials read, sums and zero rows written
+    fused: bool = False
 
 
 def bwd_cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causal: bool = True,
@@ -122,7 +128,10 @@ def bwd_cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causa
     gathers are written once as final gradients, rows several patterns
     gather once per covering pattern as fp32 partials (Dh floats per
     gradient), which the merge kernel reads back before writing the sums
-    and the zero rows of positions no pattern gathers."""
+    and the zero rows of positions no pattern gathers. When every segment
+    gathers at most 32 rows one kernel reads each gathered row's q, k, v,
+    dout, out and lse once and writes its three gradients (D is formed on
+    the way, never stored)."""
     fwd = cost(B, N, H, Dh, patterns, causal, elem_bytes)
     pairs = fwd.flops_alg / (4.0 * Dh)
     rows = fwd.gathered_rows
@@ -139,10 +148,14 @@ def bwd_cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causa
         none += int((count == 0).sum())
         multi_rows += int((count >= 2).sum())
         multi_slots += int(count[count >= 2].sum())
+    merge = B * (multi_slots * 3.0 * prow + (multi_rows + none) * 3.0 * row)
+    if max(lmax(N, w, r) for (w, r) in patterns) <= 32:
+        fused = rows * (5.0 * row + 4.0) + B * (single * 3.0 * row + multi_slots * 3.0 * prow)
+        return BwdCost(pairs, 10.0 * Dh * pairs, 10.0 * Dh * pairs, 0.0, pairs, 0.0, fused, 0.0,
+                       merge, fused=True)
     reads = rows * (4.0 * row + 8.0)
     kv_write = B * (single * 2.0 * row + multi_slots * 2.0 * prow)
     q_write = B * (single * row + multi_slots * prow)
-    merge = B * (multi_slots * 3.0 * prow + (multi_rows + none) * 3.0 * row)
     prep = B * N * H * (2.0 * row + 4.0)
     return BwdCost(pairs, 10.0 * Dh * pairs, 8.0 * Dh * pairs, 6.0 * Dh * pairs, 2.0 * pairs,
                    prep, reads + kv_write, reads + q_write, merge)

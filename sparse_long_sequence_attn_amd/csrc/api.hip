@@ -319,6 +319,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   a.k = k;
   a.v = v;
   a.dout = dout;
+  a.out = out;
   a.lse = lse;
   a.dvec = ws;
   a.dq = dq;
@@ -335,11 +336,15 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   for (int j = 0; j < pl.np; ++j) a.pat[j].po_off = pl.bwd_po_off[pl.bwd.order[j]];
 
   hipError_t e = hipSuccess;
-  if (stages & DA_BWD_PREP) e = da::launch_bwd_prep(ra, pl.bf16, st);
+  // every segment at most 32 rows: one kernel (in the KV stage) computes D,
+  // dq, dk and dv; the PREP and Q stages have nothing to do
+  const bool fused = pl.nw == 1;
+  if (!fused && (stages & DA_BWD_PREP)) e = da::launch_bwd_prep(ra, pl.bf16, st);
   if (e == hipSuccess && (stages & DA_BWD_KV))
-    e = da::launch_bwd_kv(a, pl.bf16, pl.nw, pl.causal, pl.bwd.grid, st);
-  if (e == hipSuccess && (stages & DA_BWD_Q))
-    e = da::launch_bwd_q(a, pl.bf16, pl.nw, pl.causal, pl.bwd.grid, st);
+    e = fused ? da::launch_bwd_short(a, pl.bf16, pl.causal, pl.bwd.grid, st)
+              : da::launch_bwd_kv(a, pl.bf16, pl.causal, pl.bwd.grid, st);
+  if (e == hipSuccess && !fused && (stages & DA_BWD_Q))
+    e = da::launch_bwd_q(a, pl.bf16, pl.causal, pl.bwd.grid, st);
   if (e == hipSuccess && (stages & DA_BWD_MERGE)) e = da::launch_bwd_merge(ra, pl.bf16, st);
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }

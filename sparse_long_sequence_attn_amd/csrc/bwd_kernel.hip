@@ -13,16 +13,19 @@
 // summed over the patterns that gather a row.
 //
 // Kernels:
+//  * bwd_short_kernel: when every segment gathers at most 32 rows, one wave
+//    per (pattern, batch, head, segment) unit computes D, dq, dk and dv at
+//    once; the three kernels below then have nothing to do.
 //  * bwd_prep_kernel: D for every row.
-//  * bwd_kv_kernel: one workgroup per tile of 32 * NW gathered keys of one
-//    (pattern, batch, head, segment) unit. Each wave keeps its 32 keys' K and
+//  * bwd_kv_kernel: one workgroup per tile of 128 gathered keys (4 waves of
+//    32) of one unit. Each wave keeps its 32 keys' K and
 //    V fragments and the dK^T, dV^T accumulators in registers and streams
 //    the unit's query rows (Q, dout, lse, D) through LDS, double buffered.
 //    S = Q K^T puts one key in each lane and 16 of its queries in registers,
 //    which is the B-operand layout of dV^T += dout^T P and dK^T += Q^T dS;
 //    their A operands (8 queries of one dimension per lane) come from the
 //    LDS transpose read.
-//  * bwd_q_kernel: one workgroup per tile of 32 * NW gathered queries, in the
+//  * bwd_q_kernel: one workgroup per tile of 128 gathered queries, in the
 //    forward kernel's layout (S^T = K Q^T: one query per lane), K and V
 //    streamed through LDS; dQ^T += K^T dS^T takes K^T from the transpose read.
 //  * bwd_merge_kernel: rows several patterns gather add up their fp32
@@ -126,6 +129,18 @@ struct RowFrag {
       }
     }
   }
+  // the same fragments from a row staged in LDS (row stride lds_stride<BF>)
+  template <class T>
+  __device__ inline void load_lds(const T* row, int hh) {
+    if constexpr (BF) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        x[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks + 8 * hh);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) x[ks] = row[2 * ks + hh];
+    }
+  }
 };
 
 // Stages R gathered rows of two tensors (16-byte chunks: global ->
@@ -152,6 +167,20 @@ struct PairStager {
     for (int i = 0; i < CK; ++i) {
       ra[i] = dev_load16(sa, base + off[i]);
       rb[i] = dev_load16(sb, base + off[i]);
+    }
+  }
+  __device__ inline void store_first(int tid, T* A) const {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int c = tid + i * NT;
+      const int row = c / kChunksPerRow, ch = c % kChunksPerRow;
+      if constexpr (BF) {
+        *reinterpret_cast<u32x4*>(A + row * ST + ch * 8) = ra[i];
+      } else {
+        float* da = reinterpret_cast<float*>(A) + row * ST + 4 * ch;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) da[e] = __uint_as_float(ra[i][e]);
+      }
     }
   }
   __device__ inline void store(int tid, T* A, T* B) const {
@@ -263,8 +292,9 @@ __device__ inline void write_rows(const float* srow, const int32_t* mpos, const 
 
 template <int NW, bool CAUSAL, bool BF>
 __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
+  static_assert(NW == 4, "segments of at most 32 rows take bwd_short_kernel");
   using T = typename std::conditional<BF, __bf16, float>::type;
-  constexpr int BQ = NW == 4 ? 64 : 32;  // query rows per LDS tile
+  constexpr int BQ = 64;  // query rows per LDS tile
   constexpr int QBT = BQ / 32;
   constexpr int NT = 64 * NW;
   constexpr int ST = lds_stride<BF>();
@@ -272,7 +302,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int kTileBytes = kTileElems * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dout, lse2, D
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
-  static_assert(NW != 1 || 2 * kBufBytes >= kStageBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
 
   UnitTile tl;
@@ -440,42 +469,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
   const PatDev& P = a.pat[tl.p];
   const int64_t slots = P.units * P.lmax;
   const int64_t prow0 = (g.bh * P.nseg + tl.seg) * P.lmax;  // the unit's first slot
-  if constexpr (NW == 1) {
-    // the tiles are consumed (the loop ended with a barrier); one tensor at
-    // a time through the staging area
-    float* const srow = reinterpret_cast<float*>(smem);
-    int32_t* const mpos = reinterpret_cast<int32_t*>(srow + 32 * kStageStride);
-    int32_t* const mkind = mpos + 32;
-    if (hh == 0) {
-      int32_t kind = 0, pos32 = -1;
-      if (mk < g.L) {
-        const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
-        pos32 = (int32_t)pos;  // positions are below 2^31
-        kind = coverage(a, (uint32_t)pos, tl.h) == 1 ? 1 : 2;
-      }
-      mpos[n] = pos32;
-      mkind[n] = kind;
-    }
-    stage_row(srow, dK, a.scale, n, hh);
-    __syncthreads();
-    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs,
-                   a.ws + P.po_off + (slots + prow0 + kw0) * kDh, lane);
-    __syncthreads();
-    stage_row(srow, dV, 1.f, n, hh);
-    __syncthreads();
-    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dv) + g.headbase, g.rs,
-                   a.ws + P.po_off + (2 * slots + prow0 + kw0) * kDh, lane);
+  if (mk >= g.L) return;
+  const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
+  if (coverage(a, (uint32_t)pos, tl.h) == 1) {
+    const int64_t e = g.headbase + pos * g.rs;
+    put_row<BF>(a.dk, e, dK, a.scale, hh);
+    put_row<BF>(a.dv, e, dV, 1.f, hh);
   } else {
-    if (mk >= g.L) return;
-    const int64_t pos = g.seg0 + g.off + (int64_t)mk * g.r;
-    if (coverage(a, (uint32_t)pos, tl.h) == 1) {
-      const int64_t e = g.headbase + pos * g.rs;
-      put_row<BF>(a.dk, e, dK, a.scale, hh);
-      put_row<BF>(a.dv, e, dV, 1.f, hh);
-    } else {
-      put_partial(a.ws + P.po_off + (slots + prow0 + mk) * kDh, dK, a.scale, hh);
-      put_partial(a.ws + P.po_off + (2 * slots + prow0 + mk) * kDh, dV, 1.f, hh);
-    }
+    put_partial(a.ws + P.po_off + (slots + prow0 + mk) * kDh, dK, a.scale, hh);
+    put_partial(a.ws + P.po_off + (2 * slots + prow0 + mk) * kDh, dV, 1.f, hh);
   }
 }
 
@@ -483,15 +485,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
 
 template <int NW, bool CAUSAL, bool BF>
 __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
+  static_assert(NW == 4, "segments of at most 32 rows take bwd_short_kernel");
   using T = typename std::conditional<BF, __bf16, float>::type;
-  constexpr int BK = NW == 4 ? 64 : 32;  // key rows per LDS tile
+  constexpr int BK = 64;  // key rows per LDS tile
   constexpr int KBT = BK / 32;
   constexpr int NT = 64 * NW;
   constexpr int ST = lds_stride<BF>();
   constexpr int kTileBytes = BK * ST * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes;  // K, V
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
-  static_assert(NW != 1 || 2 * kBufBytes >= kStageBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
 
   UnitTile tl;
@@ -629,28 +631,231 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
 
   const PatDev& P = a.pat[tl.p];
   const int64_t prow0 = (g.bh * P.nseg + tl.seg) * P.lmax;  // the unit's first slot
-  if constexpr (NW == 1) {
-    float* const srow = reinterpret_cast<float*>(smem);
-    int32_t* const mpos = reinterpret_cast<int32_t*>(srow + 32 * kStageStride);
-    int32_t* const mkind = mpos + 32;
-    if (hh == 0) {
-      int32_t kind = 0;
-      if (mq < g.L) kind = coverage(a, (uint32_t)pos, tl.h) == 1 ? 1 : 2;
-      mpos[n] = mq < g.L ? (int32_t)pos : -1;  // positions are below 2^31
-      mkind[n] = kind;
-    }
-    stage_row(srow, dQ, a.scale, n, hh);
-    __syncthreads();
-    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs,
-                   a.ws + P.po_off + (prow0 + qw0) * kDh, lane);
+  if (mq >= g.L) return;
+  if (coverage(a, (uint32_t)pos, tl.h) == 1) {
+    put_row<BF>(a.dq, g.headbase + pos * g.rs, dQ, a.scale, hh);
   } else {
-    if (mq >= g.L) return;
-    if (coverage(a, (uint32_t)pos, tl.h) == 1) {
-      put_row<BF>(a.dq, g.headbase + pos * g.rs, dQ, a.scale, hh);
-    } else {
-      put_partial(a.ws + P.po_off + (prow0 + mq) * kDh, dQ, a.scale, hh);
+    put_partial(a.ws + P.po_off + (prow0 + mq) * kDh, dQ, a.scale, hh);
+  }
+}
+
+// ---------------------------------------------------------------- short segments
+
+// Segments of at most 32 gathered rows: one wave takes a whole unit, every
+// query and key of it at once, and computes all three gradients, so q, k, v,
+// dout and out are each read once. D comes from out and dout on the way in.
+// S = Q K^T and dP = dout V^T put one key in each lane (the dK/dV kernel's
+// layout); dV^T = dout^T P and dK^T = Q^T dS follow as there. dS^T is then
+// written to LDS, and dQ^T = K^T dS^T takes both operands from transpose
+// reads (K^T of the staged K, dS of the staged dS^T). Rows are written
+// through the LDS staging area as 128-byte lines.
+template <bool CAUSAL, bool BF>
+__global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  constexpr int ST = lds_stride<BF>();
+  constexpr int kTileBytes = 32 * ST * (int)sizeof(T);
+  constexpr int kBytes = 3 * kTileBytes + 2 * 32 * 4;  // Q, dout then dS^T, K; lse2, D
+  static_assert(kTileBytes % 16 == 0, "LDS alignment");
+  static_assert(3 * kTileBytes >= kStageBytes, "epilogue staging fits the tiles");
+  __shared__ __attribute__((aligned(16))) char smem[kBytes];
+  T* const Qs = reinterpret_cast<T*>(smem);
+  T* const Ds = reinterpret_cast<T*>(smem + kTileBytes);  // dout, later dS^T
+  T* const Ks = reinterpret_cast<T*>(smem + 2 * kTileBytes);
+  float* const ls = reinterpret_cast<float*>(smem + 3 * kTileBytes);
+  float* const dd = ls + 32;
+
+  UnitTile tl;
+  if (!decode_unit_tile<false>(a, blockIdx.x, &tl)) return;
+  const UnitGeom g = unit_geom<T>(a, tl);
+
+  const int lane = threadIdx.x;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t rowbase = g.headbase + (g.seg0 + g.off) * g.rs;
+  const auto rq = dev_rsrc(reinterpret_cast<const T*>(a.q) + rowbase, g.range);
+  const auto rk = dev_rsrc(reinterpret_cast<const T*>(a.k) + rowbase, g.range);
+  const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, g.range);
+  const auto rdo = dev_rsrc(reinterpret_cast<const T*>(a.dout) + rowbase, g.range);
+  const auto ro = dev_rsrc(reinterpret_cast<const T*>(a.out) + rowbase, g.range);
+
+  // rows past L load as zeros: D = 0 there, and lse2 = +inf makes P = 0
+  using Stg = PairStager<BF, 32, 64>;
+  Stg sqd, sko;
+  sqd.init(lane, g.mbytes);
+  sko.init(lane, g.mbytes);
+  sqd.load(rq, rdo, 0);
+  sko.load(rk, ro, 0);
+  RowFrag<BF> vf;  // B operand of dP = dout V^T
+  vf.load(rv, (uint32_t)n * g.mbytes, hh);
+  int64_t pos = 0;
+  float l2 = INFINITY;
+  if (n < g.L) {
+    pos = g.seg0 + g.off + (int64_t)n * g.r;
+    l2 = a.lse[g.bh * a.N + pos] * kLog2e;
+  }
+  // D: each chunk's share of dout . out, summed over the chunks of its row
+  // (lanes with the same lane / kChunksPerRow)
+  constexpr int CPR = Stg::kChunksPerRow;
+#pragma unroll
+  for (int i = 0; i < Stg::CK; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t o = sko.rb[i][e], d = sqd.rb[i][e];
+      if constexpr (BF) {
+        s = fmaf(__uint_as_float(o << 16), __uint_as_float(d << 16), s);
+        s = fmaf(__uint_as_float(o & 0xffff0000u), __uint_as_float(d & 0xffff0000u), s);
+      } else {
+        s = fmaf(__uint_as_float(o), __uint_as_float(d), s);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < CPR; m *= 2) s += __shfl_xor(s, m);
+    if (lane % CPR == 0) dd[(lane + 64 * i) / CPR] = s;
+  }
+  sqd.store(lane, Qs, Ds);
+  sko.store_first(lane, Ks);
+  if (hh == 0) ls[n] = l2;
+  __syncthreads();
+
+  RowFrag<BF> kf;  // B operand of S = Q K^T
+  kf.load_lds(Ks + n * ST, hh);
+  f32x16 S, dP;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) S[v] = dP[v] = 0.f;
+  if constexpr (BF) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + n * ST + 16 * ks + 8 * hh);
+      const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + n * ST + 16 * ks + 8 * hh);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf.x[ks], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf.x[ks], dP, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      S = __builtin_amdgcn_mfma_f32_32x32x2f32(Qs[n * ST + 2 * ks + hh], kf.x[ks], S, 0, 0, 0);
+      dP = __builtin_amdgcn_mfma_f32_32x32x2f32(Ds[n * ST + 2 * ks + hh], vf.x[ks], dP, 0, 0, 0);
     }
   }
+  // register v: query 8(v/4) + 4hh + v%4, key n; causal: the whole unit is
+  // the diagonal block
+  float pv[16], sv[16];
+  const float sl2 = a.sl2;
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    const int qi = 8 * gq + 4 * hh;
+    const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qi);
+    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + qi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int v = 4 * gq + j;
+      float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l4[j]));
+      if (CAUSAL && qi + j < n) p = 0.f;
+      pv[v] = p;
+      sv[v] = p * (dP[v] - d4[j]);
+    }
+  }
+
+  f32x16 dK[2], dV[2], dQ[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dK[db][v] = dV[db][v] = dQ[db][v] = 0.f;
+  const uint32_t trl = tr_lane_offset<ST>(lane);
+  if constexpr (BF) {
+    const lds_cptr qbase = (lds_cptr)smem;
+    const lds_cptr dbase = qbase + kTileBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 pb = to_bf16x8(pv + 8 * c);
+      const bf16x8 sb = to_bf16x8(sv + 8 * c);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const uint32_t o = trl + (uint32_t)(16 * c * ST + db * 32) * 2;
+        dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(dbase, o, ST), pb, dV[db], 0,
+                                                         0, 0);
+        dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qbase, o, ST), sb, dK[db], 0,
+                                                         0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int qi = 8 * (v >> 2) + 4 * hh + (v & 3);
+        dV[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ds[qi * ST + db * 32 + n], pv[v], dV[db], 0,
+                                                      0, 0);
+        dK[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Qs[qi * ST + db * 32 + n], sv[v], dK[db], 0,
+                                                      0, 0);
+      }
+  }
+  __syncthreads();  // dout consumed: its tile takes dS^T (row = key n)
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    T* dst = Ds + n * ST + 8 * gq + 4 * hh;
+    if constexpr (BF) {
+      *reinterpret_cast<u32x2*>(dst) = u32x2{dev_pack_bf16(sv[4 * gq], sv[4 * gq + 1]),
+                                             dev_pack_bf16(sv[4 * gq + 2], sv[4 * gq + 3])};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[j] = sv[4 * gq + j];
+    }
+  }
+  __syncthreads();
+  // dQ^T[dim][query] += K^T[dim][key] dS^T[key][query]
+  if constexpr (BF) {
+    const lds_cptr sbase = (lds_cptr)smem + kTileBytes;
+    const lds_cptr kbase = (lds_cptr)smem + 2 * kTileBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 sb = tr_fragment(sbase, trl + (uint32_t)(16 * c * ST) * 2, ST);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const uint32_t o = trl + (uint32_t)(16 * c * ST + db * 32) * 2;
+        dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(kbase, o, ST), sb, dQ[db], 0,
+                                                         0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ki = 8 * (v >> 2) + 4 * hh + (v & 3);
+        dQ[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Ks[ki * ST + db * 32 + n], Ds[ki * ST + n],
+                                                      dQ[db], 0, 0, 0);
+      }
+  }
+  __syncthreads();  // tiles consumed: the staging area takes their place
+
+  const PatDev& P = a.pat[tl.p];
+  const int64_t slots = P.units * P.lmax;
+  const int64_t prow0 = (g.bh * P.nseg + tl.seg) * P.lmax;  // the unit's first slot
+  float* const srow = reinterpret_cast<float*>(smem);
+  int32_t* const mpos = reinterpret_cast<int32_t*>(srow + 32 * kStageStride);
+  int32_t* const mkind = mpos + 32;
+  if (hh == 0) {
+    int32_t kind = 0;
+    if (n < g.L) kind = coverage(a, (uint32_t)pos, tl.h) == 1 ? 1 : 2;
+    mpos[n] = n < g.L ? (int32_t)pos : -1;  // positions are below 2^31
+    mkind[n] = kind;
+  }
+  float* const part = a.ws + P.po_off + prow0 * kDh;
+  stage_row(srow, dQ, a.scale, n, hh);
+  __syncthreads();
+  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, part, lane);
+  __syncthreads();
+  stage_row(srow, dK, a.scale, n, hh);
+  __syncthreads();
+  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs,
+                 part + slots * kDh, lane);
+  __syncthreads();
+  stage_row(srow, dV, 1.f, n, hh);
+  __syncthreads();
+  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dv) + g.headbase, g.rs,
+                 part + 2 * slots * kDh, lane);
 }
 
 // ---------------------------------------------------------------- row passes
@@ -794,6 +999,16 @@ hipError_t launch_q_cfg(const BwdArgs& a, bool causal, int64_t grid, hipStream_t
   return hipGetLastError();
 }
 
+template <bool BF>
+hipError_t launch_short_cfg(const BwdArgs& a, bool causal, int64_t grid, hipStream_t st) {
+  const dim3 g((uint32_t)grid), b(64);
+  if (causal)
+    hipLaunchKernelGGL((bwd_short_kernel<true, BF>), g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_short_kernel<false, BF>), g, b, 0, st, a);
+  return hipGetLastError();
+}
+
 dim3 row_grid(const BwdRowArgs& a) {
   const int64_t rows = a.N * a.H;
   return dim3((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B);
@@ -810,20 +1025,20 @@ hipError_t launch_bwd_prep(const BwdRowArgs& a, bool bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
-                         hipStream_t st) {
-  if (bf16) return nw == 4 ? launch_kv_cfg<4, true>(a, causal, grid, st)
-                           : launch_kv_cfg<1, true>(a, causal, grid, st);
-  return nw == 4 ? launch_kv_cfg<4, false>(a, causal, grid, st)
-                 : launch_kv_cfg<1, false>(a, causal, grid, st);
+hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st) {
+  return bf16 ? launch_kv_cfg<4, true>(a, causal, grid, st)
+              : launch_kv_cfg<4, false>(a, causal, grid, st);
 }
 
-hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
-                        hipStream_t st) {
-  if (bf16) return nw == 4 ? launch_q_cfg<4, true>(a, causal, grid, st)
-                           : launch_q_cfg<1, true>(a, causal, grid, st);
-  return nw == 4 ? launch_q_cfg<4, false>(a, causal, grid, st)
-                 : launch_q_cfg<1, false>(a, causal, grid, st);
+hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st) {
+  return bf16 ? launch_q_cfg<4, true>(a, causal, grid, st)
+              : launch_q_cfg<4, false>(a, causal, grid, st);
+}
+
+hipError_t launch_bwd_short(const BwdArgs& a, bool bf16, bool causal, int64_t grid,
+                            hipStream_t st) {
+  return bf16 ? launch_short_cfg<true>(a, causal, grid, st)
+              : launch_short_cfg<false>(a, causal, grid, st);
 }
 
 hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st) {

@@ -19,6 +19,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const void* dout;
+  const void* out;    // read only by the short-segment kernel (for D)
   const float* lse;   // [B, H, N], natural log, from the forward pass
   const float* dvec;  // [B, H, N], D = dout . out per row
   void* dq;

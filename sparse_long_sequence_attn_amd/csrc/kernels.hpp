@@ -20,13 +20,15 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, b
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st);
 
 // Backward pass (bwd_kernel.hip): D = dout . out per row; dK and dV per
-// key tile; dQ per query tile (tiles of 32 * nw gathered rows, the
-// attention launch's tile order and grid); the partial sums and zero rows.
+// key tile; dQ per query tile (tiles of 128 gathered rows, the attention
+// launch's tile order, nw = 4); the partial sums and zero rows.
 hipError_t launch_bwd_prep(const BwdRowArgs& a, bool bf16, hipStream_t st);
-hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
-                         hipStream_t st);
-hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, int nw, bool causal, int64_t grid,
-                        hipStream_t st);
+hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st);
+hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st);
+// Segments of at most 32 gathered rows (nw = 1): dq, dk, dv and D in one
+// kernel, one wave per unit.
+hipError_t launch_bwd_short(const BwdArgs& a, bool bf16, bool causal, int64_t grid,
+                            hipStream_t st);
 hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st);
 
 // qk_norm (qknorm_kernel.hip): blocks per tensor for `rows` rows; forward;
