@@ -461,6 +461,10 @@ attn_fwd_kernel(const AttnArgs a) {
   // ---- main loop over key tiles, double-buffered through LDS
   load_tile(0);
   store_tile(0);
+  // every load issued so far (the query fragments included) completes here:
+  // otherwise the loop's first use of the fragments waits on the global
+  // loads the loop itself has just issued for the next tile
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (NBUF == 2) {
     for (int kt = 0; kt < nkt; ++kt) {

@@ -342,7 +342,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
 
   PairStager<BF, BQ, NT> stg;
   stg.init(tid, g.mbytes);
-  float lreg = 0.f, dreg = 0.f;  // lse2 and D of query row tid of the next tile
+  // lse and D of query row tid of the next tile; lse is scaled to log2 only
+  // when stored, since using a loaded value right away would make the wave
+  // wait for the tile loads issued just before it
+  float lreg = 0.f, dreg = 0.f;
   auto load_tile = [&](int t) {
     const int32_t m0 = qstart + t * BQ;
     stg.load(rq, rdo, (uint32_t)m0 * g.mbytes);
@@ -352,7 +355,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
       dreg = 0.f;
       if (m < g.L) {
         const int64_t pos = g.seg0 + g.off + (int64_t)m * g.r;
-        lreg = lse_row[pos] * kLog2e;
+        lreg = lse_row[pos];
         dreg = d_row[pos];
       }
     }
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
     stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
     if (tid < BQ) {
       float* ls = reinterpret_cast<float*>(base + 2 * kTileBytes);
-      ls[tid] = lreg;
+      ls[tid] = lreg * kLog2e;
       ls[BQ + tid] = dreg;
     }
   };
