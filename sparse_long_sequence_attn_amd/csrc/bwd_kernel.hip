@@ -291,10 +291,11 @@ __device__ inline void write_rows(const float* srow, const int32_t* mpos, const 
 // ---------------------------------------------------------------- dK, dV
 
 template <int NW, bool CAUSAL, bool BF>
-__global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
+// bf16: at least 3 waves per SIMD (the fragments of K and V live in LDS)
+__global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdArgs a) {
   static_assert(NW == 4, "segments of at most 32 rows take bwd_short_kernel");
   using T = typename std::conditional<BF, __bf16, float>::type;
-  constexpr int BQ = 64;  // query rows per LDS tile
+  constexpr int BQ = 32;  // query rows per LDS tile
   constexpr int QBT = BQ / 32;
   constexpr int NT = 64 * NW;
   constexpr int ST = lds_stride<BF>();
@@ -302,7 +303,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
   constexpr int kTileBytes = kTileElems * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dout, lse2, D
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
-  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
+  // bf16: the workgroup's 32 * NW V rows stay in LDS (128-byte rows, 16-byte
+  // chunk j of row x at slot j ^ ((x >> 1) & 7)) instead of registers
+  constexpr int kVBytes = BF ? 32 * NW * kDh * 2 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes + 2 * kVBytes];
+  T* const Vl = reinterpret_cast<T*>(smem + 2 * kBufBytes);
+  T* const Kl = reinterpret_cast<T*>(smem + 2 * kBufBytes + kVBytes);
 
   UnitTile tl;
   if (!decode_unit_tile<false>(a, blockIdx.x, &tl)) return;
@@ -329,6 +335,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
   RowFrag<BF> kf, vf;                // B operands of S = Q K^T and dP = dout V^T
   kf.load(rk, (uint32_t)mk * g.mbytes, hh);
   vf.load(rv, (uint32_t)mk * g.mbytes, hh);
+  const int vrow = wv * 32 + n;
+  if constexpr (BF) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int o = vrow * kDh + (((2 * ks + hh) ^ ((vrow >> 1) & 7)) << 3);
+      *reinterpret_cast<bf16x8*>(Vl + o) = vf.x[ks];
+      *reinterpret_cast<bf16x8*>(Kl + o) = kf.x[ks];
+    }
+  }
 
   f32x16 dK[2], dV[2];
 #pragma unroll
@@ -393,8 +408,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
         for (int ks = 0; ks < 4; ++ks) {
           const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + row * ST + 16 * ks + 8 * hh);
           const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + row * ST + 16 * ks + 8 * hh);
-          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf.x[ks], S, 0, 0, 0);
-          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf.x[ks], dP, 0, 0, 0);
+          const int o = vrow * kDh + (((2 * ks + hh) ^ ((vrow >> 1) & 7)) << 3);
+          const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kl + o);
+          S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, S, 0, 0, 0);
+          const bf16x8 vb = *reinterpret_cast<const bf16x8*>(Vl + o);
+          dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dP, 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -407,6 +425,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
       }
       // register v: query qb*32 + 8(v/4) + 4hh + v%4 of the tile, key n
       float pv[16], sv[16];
+      u32x4 pk[2], sk[2];  // bf16 P and dS, packed as they are formed
       auto probs = [&](bool diag) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -421,6 +440,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
             pv[v] = p;
             sv[v] = p * (dP[v] - d4[j]);
           }
+          if constexpr (BF) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int v = 4 * gq + 2 * j;
+              pk[gq >> 1][2 * (gq & 1) + j] = dev_pack_bf16(pv[v], pv[v + 1]);
+              sk[gq >> 1][2 * (gq & 1) + j] = dev_pack_bf16(sv[v], sv[v + 1]);
+            }
+          }
         }
       };
       if (CAUSAL && qs == kw0)  // the diagonal block: keys after their query masked
@@ -432,8 +459,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_kv_kernel(const BwdArgs a) {
         const lds_cptr dbase = qbase + kTileBytes;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const bf16x8 pb = to_bf16x8(pv + 8 * c);
-          const bf16x8 sb = to_bf16x8(sv + 8 * c);
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[c]);
+          const bf16x8 sb = __builtin_bit_cast(bf16x8, sk[c]);
 #pragma unroll
           for (int db = 0; db < 2; ++db) {
             const uint32_t o = trl + (uint32_t)((qb * 32 + 16 * c) * ST + db * 32) * 2;
