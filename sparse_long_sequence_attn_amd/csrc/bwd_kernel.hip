@@ -18,9 +18,10 @@
 //    once; the three kernels below then have nothing to do.
 //  * bwd_prep_kernel: D for every row.
 //  * bwd_kv_kernel: one workgroup per tile of 128 gathered keys (4 waves of
-//    32) of one unit. Each wave keeps its 32 keys' K and
-//    V fragments and the dK^T, dV^T accumulators in registers and streams
-//    the unit's query rows (Q, dout, lse, D) through LDS, double buffered.
+//    32) of one unit. Each wave keeps the dK^T, dV^T accumulators of its 32
+//    keys in registers, reads its keys' K and V fragments from LDS (bf16;
+//    registers for fp32) and streams the unit's query rows (Q, dout, lse, D)
+//    through LDS, double buffered, 32 rows per stage.
 //    S = Q K^T puts one key in each lane and 16 of its queries in registers,
 //    which is the B-operand layout of dV^T += dout^T P and dK^T += Q^T dS;
 //    their A operands (8 queries of one dimension per lane) come from the
@@ -243,8 +244,8 @@ __device__ inline void put_partial(float* dst, const f32x16 (&acc)[2], float mul
     }
 }
 
-// Row-contiguous writes for one-wave workgroups (segments of at most 32
-// rows, where the kernels are bound by their writes): each lane stages its
+// Row-contiguous writes for the short-segment kernel (one wave per unit of
+// at most 32 rows, bound by its memory traffic): each lane stages its
 // half row (MFMA layout) in LDS, then 16 lanes write each of the wave's 32
 // rows as one contiguous line - 128 bytes of bf16 (256 of fp32) - instead of
 // 8-byte pieces of 32 rows per store.

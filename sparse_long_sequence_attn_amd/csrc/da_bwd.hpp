@@ -7,8 +7,9 @@ namespace da {
 
 // Backward launch over every tile of every pattern. The tile order is the
 // forward's (units dealt to XCDs round-robin, patterns sorted by ntile,
-// descending); ntile counts tiles of 32 * NW gathered rows, keys for the
-// dK/dV kernel and queries for the dQ kernel.
+// descending); ntile counts tiles of 32 * NW gathered rows (NW = 4: keys
+// for the dK/dV kernel, queries for the dQ kernel; NW = 1: whole units of
+// the short-segment kernel).
 //
 // Partial slots: a pattern with po_off >= 0 keeps, at float offset po_off of
 // ws, three blocks of units * lmax rows of kDh floats (dq, dk, dv in that

@@ -25,8 +25,8 @@ hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_bwd_prep(const BwdRowArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st);
 hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st);
-// Segments of at most 32 gathered rows (nw = 1): dq, dk, dv and D in one
-// kernel, one wave per unit.
+// Segments of at most 32 gathered rows (the plan's one-wave case): dq, dk,
+// dv and D in one kernel, one wave per unit.
 hipError_t launch_bwd_short(const BwdArgs& a, bool bf16, bool causal, int64_t grid,
                             hipStream_t st);
 hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st);
