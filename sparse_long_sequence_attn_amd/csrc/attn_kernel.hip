@@ -59,7 +59,18 @@ __device__ inline bool decode_tile(const AttnArgs& a, int64_t id, Tile* t) {
     const int64_t cnt = first < u1 ? (u1 - first + kXcds - 1) / kXcds : 0;
     const int64_t nt = a.pat[p].ntile;
     if (slot < cnt * nt) {
-      const int64_t lu = slot / nt;
+      // groups of G units (their key/value rows fill about an XCD's L2),
+      // heaviest tiles of the group first
+      constexpr int64_t G = 4;
+      const int64_t gfull = cnt / G;
+      int64_t gi = slot / (G * nt), gsz = G;
+      if (gi >= gfull) {
+        gi = gfull;
+        gsz = cnt - gfull * G;
+      }
+      const int64_t r0 = slot - gi * G * nt;
+      const int64_t k = r0 / gsz;
+      const int64_t lu = gi * G + r0 % gsz;
       const int64_t rem = first + lu * kXcds - u0;  // unit index inside the pattern
       const int64_t nseg = a.pat[p].nseg;
       t->seg = rem % nseg;
@@ -67,7 +78,7 @@ __device__ inline bool decode_tile(const AttnArgs& a, int64_t id, Tile* t) {
       t->h = (int32_t)(bh % a.H);
       t->b = bh / a.H;
       t->p = p;
-      t->qt = (int32_t)(nt - 1 - (slot - lu * nt));
+      t->qt = (int32_t)(nt - 1 - k);
       return true;
     }
     slot -= cnt * nt;

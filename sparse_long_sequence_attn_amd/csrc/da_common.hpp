@@ -54,11 +54,14 @@ struct PatDev {
 
 // Attention launch. Tiles of all patterns share one grid. Block ids are
 // dealt to the chip's XCDs round-robin (id mod kXcds), so the tiles are laid
-// out per XCD: each XCD walks its own list of (batch, head, segment) units,
-// all query tiles of a unit next to each other, heaviest (last) tile first.
-// Tiles of one unit then run at the same time on one XCD and read the same
-// key/value rows through that XCD's L2. Patterns are stored sorted by ntile
-// (descending); units are handed to XCDs round-robin in that order.
+// out per XCD: each XCD gets its share of every pattern's (batch, head,
+// segment) units and walks them in groups of 4 units, heaviest tiles of the
+// group first (the last query tile of each unit, then the one before it,
+// and so on). A group's key/value rows about fill the XCD's L2, and the
+// shortest tiles come last, so the XCD's workgroup slots drain together
+// instead of waiting on the long tiles of the final units. Patterns are
+// stored sorted by ntile (descending); units are handed to XCDs round-robin
+// in that order.
 constexpr int kXcds = 8;
 
 struct AttnArgs {
