@@ -60,8 +60,9 @@ __device__ inline bool decode_tile(const AttnArgs& a, int64_t id, Tile* t) {
     const int64_t nt = a.pat[p].ntile;
     if (slot < cnt * nt) {
       // groups of G units (their key/value rows fill about an XCD's L2),
-      // heaviest tiles of the group first
-      constexpr int64_t G = 4;
+      // heaviest tiles of the group first; the last pattern's units form
+      // one group, so the XCD's list ends with its shortest tiles
+      const int64_t G = p == a.np - 1 ? (cnt > 0 ? cnt : 1) : 4;
       const int64_t gfull = cnt / G;
       int64_t gi = slot / (G * nt), gsz = G;
       if (gi >= gfull) {

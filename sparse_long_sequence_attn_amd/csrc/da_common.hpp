@@ -57,9 +57,10 @@ struct PatDev {
 // out per XCD: each XCD gets its share of every pattern's (batch, head,
 // segment) units and walks them in groups of 4 units, heaviest tiles of the
 // group first (the last query tile of each unit, then the one before it,
-// and so on). A group's key/value rows about fill the XCD's L2, and the
-// shortest tiles come last, so the XCD's workgroup slots drain together
-// instead of waiting on the long tiles of the final units. Patterns are
+// and so on); the last pattern's units form one group. A group's key/value
+// rows about fill the XCD's L2, and the list ends with its shortest tiles,
+// so the XCD's workgroup slots drain together instead of waiting on the
+// long tiles of the final units. Patterns are
 // stored sorted by ntile (descending); units are handed to XCDs round-robin
 // in that order.
 constexpr int kXcds = 8;
