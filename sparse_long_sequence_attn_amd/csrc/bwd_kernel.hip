@@ -961,8 +961,11 @@ __global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(const BwdRowArgs 
 
 // Sum of the per-pattern partials of rows two or more patterns gather; zero
 // gradients for rows no pattern gathers. Rows one pattern gathers were
-// written by the dK/dV and dQ kernels.
-template <bool BF>
+// written by the dK/dV and dQ kernels (or the short-segment kernel). For
+// each gradient in turn, every covering pattern's partial is loaded before
+// any is added, so a row costs three memory round trips rather than one per
+// pattern and gradient; instantiated per pattern count.
+template <bool BF, int NP>
 __global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs a,
                                                                const FastDiv h_div) {
   const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
@@ -972,42 +975,44 @@ __global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs
   const int32_t h = (int32_t)(row - t * (uint32_t)a.H);
   const int64_t b = blockIdx.y;
 
-  int32_t ci[kMaxPat];
+  int32_t ci[NP];
   int cover = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPat; ++i) {
-    ci[i] = i < a.np ? (int32_t)compact_index(t, a.pat[i], head_offset(h, a.pat[i].r)) : -1;
+  for (int i = 0; i < NP; ++i) {
+    ci[i] = (int32_t)compact_index(t, a.pat[i], head_offset(h, a.pat[i].r));
     cover += ci[i] >= 0;
   }
   if (cover == 1) return;
 
-  float acc[3][kDimsPerLane];
+  const int64_t elem = ((b * a.N + t) * a.H + h) * kDh + kDimsPerLane * sub;
+  void* const dst[3] = {a.dq, a.dk, a.dv};
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
+  for (int w = 0; w < 3; ++w) {
+    f32x4 x[NP][4];
 #pragma unroll
-    for (int i = 0; i < kDimsPerLane; ++i) acc[w][i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxPat; ++i) {
-    if (ci[i] < 0) continue;
-    const PatDev& P = a.pat[i];
-    const int64_t slots = P.units * P.lmax;
-    const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
-#pragma unroll
-    for (int w = 0; w < 3; ++w) {
+    for (int i = 0; i < NP; ++i) {
+      if (ci[i] < 0) continue;
+      const PatDev& P = a.pat[i];
+      const int64_t slots = P.units * P.lmax;
+      const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
       const f32x4* src = reinterpret_cast<const f32x4*>(a.ws + P.po_off + (w * slots + prow) * kDh +
                                                         kDimsPerLane * sub);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 x = src[j];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[w][4 * j + e] += x[e];
-      }
+      for (int j = 0; j < 4; ++j) x[i][j] = src[j];
     }
+    float acc[kDimsPerLane];
+#pragma unroll
+    for (int e = 0; e < kDimsPerLane; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (ci[i] < 0) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * j + e] += x[i][j][e];
+    }
+    store16<BF>(dst[w], elem, acc);
   }
-  const int64_t elem = ((b * a.N + t) * a.H + h) * kDh + kDimsPerLane * sub;
-  store16<BF>(a.dq, elem, acc[0]);
-  store16<BF>(a.dk, elem, acc[1]);
-  store16<BF>(a.dv, elem, acc[2]);
 }
 
 template <int NW, bool BF>
@@ -1045,6 +1050,15 @@ dim3 row_grid(const BwdRowArgs& a) {
   return dim3((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B);
 }
 
+template <bool BF, int NP = 1>
+hipError_t launch_bwd_merge_np(const BwdRowArgs& a, const FastDiv& hd, hipStream_t st) {
+  if constexpr (NP < kMaxPat) {
+    if (a.np > NP) return launch_bwd_merge_np<BF, NP + 1>(a, hd, st);
+  }
+  hipLaunchKernelGGL((bwd_merge_kernel<BF, NP>), row_grid(a), dim3(kRowThreads), 0, st, a, hd);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_bwd_prep(const BwdRowArgs& a, bool bf16, hipStream_t st) {
@@ -1074,11 +1088,7 @@ hipError_t launch_bwd_short(const BwdArgs& a, bool bf16, bool causal, int64_t gr
 
 hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st) {
   const FastDiv hd = make_fastdiv((uint32_t)a.H);
-  if (bf16)
-    hipLaunchKernelGGL(bwd_merge_kernel<true>, row_grid(a), dim3(kRowThreads), 0, st, a, hd);
-  else
-    hipLaunchKernelGGL(bwd_merge_kernel<false>, row_grid(a), dim3(kRowThreads), 0, st, a, hd);
-  return hipGetLastError();
+  return bf16 ? launch_bwd_merge_np<true>(a, hd, st) : launch_bwd_merge_np<false>(a, hd, st);
 }
 
 }  // namespace da

@@ -11,6 +11,9 @@
 // kernel is bound by HBM traffic: 4 lanes cooperate on one 64-wide row, each
 // moving 64 contiguous bytes of every covering pattern's partial, so one
 // wave handles 16 rows and the per-row coverage tests are shared by 4 lanes.
+// Every covering pattern's lse and partial row are loaded before any is
+// used (one memory round trip per row, not one per pattern); the kernel is
+// instantiated per pattern count so the registers fit the loads.
 #include "da_common.hpp"
 #include "kernels.hpp"
 
@@ -34,7 +37,7 @@ __device__ inline uint32_t pack_bf16(float x, float y) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-template <bool BF>
+template <bool BF, int NP>
 __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a, const FastDiv h_div) {
   // blockIdx.y = batch; rows of one batch are (t, h) pairs in output order
   const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
@@ -45,47 +48,50 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a, cons
   const int64_t b = blockIdx.y;
 
   // rows exactly one pattern gathers were written by the attention kernel
-  int32_t ci[kMaxPat];
+  int32_t ci[NP];
   int cover = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPat; ++i) {
-    ci[i] = i < a.np ? (int32_t)compact_index(t, a.pat[i], head_offset(h, a.pat[i].r)) : -1;
+  for (int i = 0; i < NP; ++i) {
+    ci[i] = (int32_t)compact_index(t, a.pat[i], head_offset(h, a.pat[i].r));
     cover += ci[i] >= 0;
   }
   if (cover == 1) return;
 
-  // one pass to find the largest lse, one to sum the weights and outputs
-  float l[kMaxPat];
-  float mx = -INFINITY;
+  // every covering pattern's lse and partial row are loaded before any of
+  // them is used, so their memory latencies overlap
+  float l[NP];
+  f32x4 src[NP][4];
 #pragma unroll
-  for (int i = 0; i < kMaxPat; ++i) {
+  for (int i = 0; i < NP; ++i) {
     l[i] = -INFINITY;
     if (ci[i] >= 0) {
       const PatDev& P = a.pat[i];
       // rows of one batch hold fewer than 2^31 slots (N * H < 2^31)
       const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
       l[i] = a.ws[P.pl_off + prow];
-      mx = fmaxf(mx, l[i]);
+      const f32x4* p =
+          reinterpret_cast<const f32x4*>(a.ws + P.po_off + prow * kDh + kDimsPerLane * sub);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) src[i][j] = p[j];
     }
   }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) mx = fmaxf(mx, l[i]);
   f32x4 acc[4] = {};
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxPat; ++i)
+    for (int i = 0; i < NP; ++i)
       if (ci[i] >= 0) s += __builtin_amdgcn_exp2f(l[i] - mx);
     const float lse2 = mx + __builtin_amdgcn_logf(s);
 #pragma unroll
-    for (int i = 0; i < kMaxPat; ++i) {
+    for (int i = 0; i < NP; ++i) {
       if (ci[i] < 0) continue;
-      const PatDev& P = a.pat[i];
-      const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
-      const f32x4* src =
-          reinterpret_cast<const f32x4*>(a.ws + P.po_off + prow * kDh + kDimsPerLane * sub);
       const float wgt = __builtin_amdgcn_exp2f(l[i] - lse2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += wgt * src[j];
+      for (int j = 0; j < 4; ++j) acc[j] += wgt * src[i][j];
     }
     lse = lse2 * kLn2;
   }
@@ -122,17 +128,22 @@ __global__ void coverage_map_kernel(const PatDev p, int32_t h, int64_t N, int64_
   out[t] = compact_index((uint32_t)t, p, head_offset(h, p.r));
 }
 
+template <bool BF, int NP = 1>
+hipError_t launch_merge_np(const MergeArgs& a, dim3 g, dim3 b, const FastDiv& hd, hipStream_t st) {
+  if constexpr (NP < kMaxPat) {
+    if (a.np > NP) return launch_merge_np<BF, NP + 1>(a, g, b, hd, st);
+  }
+  hipLaunchKernelGGL((merge_kernel<BF, NP>), g, b, 0, st, a, hd);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = a.N * a.H;
   dim3 g((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B), b(kThreads);
   const FastDiv hd = make_fastdiv((uint32_t)a.H);
-  if (bf16)
-    hipLaunchKernelGGL(merge_kernel<true>, g, b, 0, st, a, hd);
-  else
-    hipLaunchKernelGGL(merge_kernel<false>, g, b, 0, st, a, hd);
-  return hipGetLastError();
+  return bf16 ? launch_merge_np<true>(a, g, b, hd, st) : launch_merge_np<false>(a, g, b, hd, st);
 }
 
 hipError_t launch_gather_map(const PatDev& p, int32_t h, int64_t* out, hipStream_t st) {
