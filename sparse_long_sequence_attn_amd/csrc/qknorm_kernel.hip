@@ -128,35 +128,45 @@ __global__ __launch_bounds__(kThreads) void qk_norm_bwd_kernel(const QkNormArgs 
   float acc_g[kVals], acc_b[kVals];
 #pragma unroll
   for (int i = 0; i < kVals; ++i) acc_g[i] = acc_b[i] = 0.f;
-  for (int64_t r0 = blk * kRowsPerPass; r0 < a.rows; r0 += nblk * kRowsPerPass) {
-    const int64_t row = r0 + threadIdx.x / kLanesPerRow;
-    const bool valid = row < a.rows;
-    const int64_t elem = (valid ? row : 0) * kDh + kVals * sub;
-    float v[kVals], d[kVals];
-    load8<BF>(x, elem, v);
-    load8<BF>(dy, elem, d);
-    if (!valid) {
+  // two passes per iteration: both passes' loads are issued before either
+  // is used, so their memory latencies overlap
+  for (int64_t r0 = blk * kRowsPerPass; r0 < a.rows; r0 += 2 * nblk * kRowsPerPass) {
+    float v[2][kVals], d[2][kVals];
+    int64_t elem[2];
+    bool valid[2];
 #pragma unroll
-      for (int i = 0; i < kVals; ++i) d[i] = 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const int64_t row = r0 + u * nblk * kRowsPerPass + threadIdx.x / kLanesPerRow;
+      valid[u] = row < a.rows;
+      elem[u] = (valid[u] ? row : 0) * kDh + kVals * sub;
+      load8<BF>(x, elem[u], v[u]);
+      load8<BF>(dy, elem[u], d[u]);
     }
-    float mean, rstd;
-    row_stats(v, a.eps, &mean, &rstd);
-    float sg = 0.f, sgx = 0.f;
 #pragma unroll
-    for (int i = 0; i < kVals; ++i) {
-      v[i] = (v[i] - mean) * rstd;  // xh
-      const float g = d[i] * gain[i];
-      sg += g;
-      sgx = fmaf(g, v[i], sgx);
-      acc_g[i] = fmaf(d[i], v[i], acc_g[i]);
-      acc_b[i] += d[i];
+    for (int u = 0; u < 2; ++u) {
+      if (!valid[u]) {
+#pragma unroll
+        for (int i = 0; i < kVals; ++i) d[u][i] = 0.f;
+      }
+      float mean, rstd;
+      row_stats(v[u], a.eps, &mean, &rstd);
+      float sg = 0.f, sgx = 0.f;
+#pragma unroll
+      for (int i = 0; i < kVals; ++i) {
+        v[u][i] = (v[u][i] - mean) * rstd;  // xh
+        const float g = d[u][i] * gain[i];
+        sg += g;
+        sgx = fmaf(g, v[u][i], sgx);
+        acc_g[i] = fmaf(d[u][i], v[u][i], acc_g[i]);
+        acc_b[i] += d[u][i];
+      }
+      const float mg = row_sum(sg) * (1.f / kDh);
+      const float mgx = row_sum(sgx) * (1.f / kDh);
+      float o[kVals];
+#pragma unroll
+      for (int i = 0; i < kVals; ++i) o[i] = rstd * (d[u][i] * gain[i] - mg - v[u][i] * mgx);
+      if (valid[u]) store8<BF>(dx, elem[u], o);
     }
-    const float mg = row_sum(sg) * (1.f / kDh);
-    const float mgx = row_sum(sgx) * (1.f / kDh);
-    float o[kVals];
-#pragma unroll
-    for (int i = 0; i < kVals; ++i) o[i] = rstd * (d[i] * gain[i] - mg - v[i] * mgx);
-    if (valid) store8<BF>(dx, elem, o);
   }
   // block partial of dgain, dbias: rows of the block's 32 row slots, then
   // the 32 slots in order
