@@ -423,6 +423,20 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
+    # practical MFMA ceiling of this GPU for context: a dense bf16 matmul
+    a_m = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b_m = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a_m, b_m)
+    mev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    mev[0].record(stream)
+    for _ in range(10):
+        torch.matmul(a_m, b_m)
+    mev[1].record(stream)
+    torch.cuda.synchronize()
+    matmul_tflops = 2.0 * 8192 ** 3 / (mev[0].elapsed_time(mev[1]) / 10 / 1e3) / 1e12
+    del a_m, b_m
+
     c = cost(w.B, w.N, w.H, w.Dh, w.patterns, w.causal, 2 if w.dtype == "bf16" else 4)
     tokens_s = w.tokens / (ms_step / 1e3)
     peak = peak_tflops(w.dtype)
@@ -466,6 +480,8 @@ def main():
             "pct_bf16_peak_north_star_formula_step": round(100 * step_tflops_ns / peak, 2),
             "flops_algorithmic": c.flops_alg,
             "flops_north_star_formula": c.flops_ns,
+            "bf16_matmul_8192_tflops": round(matmul_tflops, 1),
+            "attn_frac_of_bf16_matmul": round(attn_tflops / matmul_tflops, 4),
             "step_ms_median": round(step_times[K // 2], 4),
             "flushed_step_ms_median": round(flushed[reps // 2], 4),
             "flushed_tokens_per_s": round(w.tokens / (flushed[reps // 2] / 1e3), 1),
