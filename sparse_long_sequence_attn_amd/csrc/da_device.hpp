@@ -53,9 +53,11 @@ struct UnitTile {
 };
 
 // Block id -> tile. Block ids are dealt to the XCDs round-robin (id mod
-// kXcds); each XCD walks its own list of units, all tiles of one unit next
-// to each other, so the tiles of a unit share that XCD's L2. Inside a unit
-// the tiles run from the last one (LAST_FIRST) or from the first one,
+// kXcds); each XCD walks its share of every pattern's units in groups of 4
+// units (their rows about fill the XCD's L2), the heaviest tiles of the
+// group first; the last pattern's units form one group, so the XCD's list
+// ends with its shortest tiles and its workgroup slots drain together. The
+// heaviest tile of a unit is its last one (LAST_FIRST) or its first one,
 // whichever carries the most work. Returns false for the padding blocks of
 // XCDs whose list is shorter than the longest one.
 template <bool LAST_FIRST, class Args>
@@ -68,7 +70,16 @@ __device__ inline bool decode_unit_tile(const Args& a, int64_t id, UnitTile* t) 
     const int64_t cnt = first < u1 ? (u1 - first + kXcds - 1) / kXcds : 0;
     const int64_t nt = a.pat[p].ntile;
     if (slot < cnt * nt) {
-      const int64_t lu = slot / nt;
+      const int64_t G = p == a.np - 1 ? (cnt > 0 ? cnt : 1) : 4;
+      const int64_t gfull = cnt / G;
+      int64_t gi = slot / (G * nt), gsz = G;
+      if (gi >= gfull) {
+        gi = gfull;
+        gsz = cnt - gfull * G;
+      }
+      const int64_t r0 = slot - gi * G * nt;
+      const int32_t k = (int32_t)(r0 / gsz);
+      const int64_t lu = gi * G + r0 % gsz;
       const int64_t rem = first + lu * kXcds - u0;
       const int64_t nseg = a.pat[p].nseg;
       t->seg = rem % nseg;
@@ -76,7 +87,6 @@ __device__ inline bool decode_unit_tile(const Args& a, int64_t id, UnitTile* t) 
       t->h = (int32_t)(bh % a.H);
       t->b = bh / a.H;
       t->p = p;
-      const int32_t k = (int32_t)(slot - lu * nt);
       t->tile = LAST_FIRST ? (int32_t)(nt - 1 - k) : k;
       return true;
     }
