@@ -97,6 +97,8 @@ BWD_CASES = [
     (1, 2048, 2, [(2048, 1)], True, None),                # 16 tiles each way
     (1, 1280, 3, [(1280, 5), (256, 1)], False, None),     # long non-causal with tails
     (2, 192, 7, [(192, 3), (192, 3)], True, None),        # a pattern listed twice
+    (1, 512, 3, [(512, 1), (256, 2), (128, 4), (64, 8), (512, 8), (256, 1), (128, 2), (64, 1)],
+     True, None),                                          # the maximum of 8 patterns
     (2, 90, 3, [(30, 1), (90, 4)], True, None),           # one-wave fused path: ragged L, partials
     (1, 50, 2, [(50, 2)], False, None),                   # one-wave fused path: L = 25, non-causal
 ]

@@ -80,6 +80,8 @@ SMALL_CASES = [
     (1, 4096, 2, [(4096, 1)], True, None),                # 32 query tiles
     (1, 2560, 3, [(2560, 5), (512, 1)], False, None),     # long non-causal with tails
     (2, 192, 7, [(192, 3), (192, 3)], True, None),        # a pattern listed twice
+    (1, 512, 3, [(512, 1), (256, 2), (128, 4), (64, 8), (512, 8), (256, 1), (128, 2), (64, 1)],
+     True, None),                                          # the maximum of 8 patterns
 ]
 
 
