@@ -144,8 +144,10 @@ int dilated_attn_fwd_merge(const void* q, const void* k, const void* v, void* ou
  * every element written. Same alignment rules as the forward pass (the
  * tensors 16-byte, lse 4-byte, workspace 256-byte aligned). dq, dk, dv and
  * the workspace must not overlap each other or any input (DA_ERR_ALIAS);
- * inputs may overlap each other. The workspace is required (it holds D) and
- * its contents on entry are ignored. */
+ * inputs may overlap each other. The workspace is required (it holds D, and
+ * the partials of rows several patterns gather; when every segment gathers
+ * at most 32 rows D stays in registers and only the partials use it) and its
+ * contents on entry are ignored. */
 
 /* Bytes of device workspace dilated_attn_bwd needs: one float per row for D
  * and, for two or more patterns, the per-pattern fp32 partial dq, dk, dv rows
