@@ -249,6 +249,17 @@ def run_module(args, dev):
                 named[names[k]].copy_(torch.from_numpy(v))
     x = torch.from_numpy(module_x(B, N, dim, c["seed"] + 1)).to(dev, torch.bfloat16)
     x.requires_grad_()
+    # the projections are library GEMMs; PyTorch's TunableOp times the
+    # library's candidate kernels for each GEMM shape on first use (here in
+    # the untimed warm-up steps) and keeps the fastest
+    tuning = args.gemm_tuning == "on" and hasattr(torch.cuda, "tunable")
+    if tuning:
+        import tempfile
+
+        torch.cuda.tunable.set_filename(os.path.join(tempfile.gettempdir(),
+                                                     "dilated_attn_tunableop.csv"))
+        torch.cuda.tunable.enable(True)
+        torch.cuda.tunable.tuning_enable(True)
     dy = torch.from_numpy(module_x(B, N, dim, c["seed"] + 2)).to(dev, torch.bfloat16)
     stream = torch.cuda.current_stream(dev)
 
@@ -257,9 +268,11 @@ def run_module(args, dev):
         x.grad = None
         mod(x).backward(dy)
 
-    for _ in range(args.warmup):
+    for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
+    if tuning:
+        torch.cuda.tunable.tuning_enable(False)  # the choices are fixed from here on
     K = args.steps
     t0 = time.perf_counter()
     for _ in range(K):
@@ -327,6 +340,8 @@ def run_module(args, dev):
             "attention_bwd_algorithmic_bytes": bc.kv_bytes + bc.q_bytes + bc.prep_bytes +
             bc.merge_bytes,
             "projection_gemm_flops": proj_flops,
+            "gemm_selection": "torch TunableOp, tuned in the warm-up steps" if tuning
+            else "library default",
             "device": torch.cuda.get_device_name(dev),
         },
     }
@@ -343,6 +358,8 @@ def main():
                     help="heads of the workload the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "module"], default="fwd")
+    ap.add_argument("--gemm-tuning", choices=["on", "off"], default="on",
+                    help="module pass: let PyTorch's TunableOp pick the projection GEMM kernels")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after the timed region, run one device copy of this many MiB "
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
