@@ -220,6 +220,49 @@ int dilated_attn_qk_norm_bwd(const void* xq, const void* xk, const void* dyq, co
                              float* dparams, int64_t rows, int32_t Dh, int32_t dtype, float eps,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ qk_norm fused
+ *
+ * The DilatedAttention module with qk_norm (LongNet package README,
+ * DilatedAttention parameters) in one pass per direction, for one pattern
+ * whose segments gather at most 32 rows (ceil(min(w, N) / r) <= 32, e.g. the
+ * README's usage example): q = qk_norm(xq), k = qk_norm(xk) as defined for
+ * dilated_attn_qk_norm_fwd are formed inside the attention kernels as rows
+ * are loaded and never stored. Any other pattern list returns
+ * DA_ERR_PATTERN; the separate dilated_attn_qk_norm_* and dilated_attn_*
+ * calls compute the same values there.
+ *
+ * xq, xk, v as q, k, v of dilated_attn_fwd (the un-normalised rows); gains
+ * and biases Dh values of dtype, 16-byte aligned, not overlapping any
+ * output; eps finite and > 0 (DA_ERR_ARG). No workspace. Other arguments,
+ * checks and outputs as dilated_attn_fwd. */
+int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
+                            const void* bias_q, const void* gain_k, const void* bias_k,
+                            float eps, void* out, float* lse, int64_t B, int64_t N, int32_t H,
+                            int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
+                            int32_t causal, int32_t dtype, float scale, void* stream);
+
+/* Device workspace bytes of dilated_attn_bwd_qknorm (the backward's own,
+ * plus per-(batch, head, segment) partial sums of the gain and bias
+ * gradients). DA_ERR_PATTERN where the fused form does not apply. */
+int dilated_attn_bwd_qknorm_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
+                                            const da_pattern* patterns, int32_t n_patterns,
+                                            int32_t dtype, size_t* bytes);
+
+/* Backward of dilated_attn_fwd_qknorm: dxq, dxk (gradients with respect to
+ * the un-normalised rows, [B, N, H, Dh] of dtype), dv, and dparams, a device
+ * float array [2][2][Dh] as for dilated_attn_qk_norm_bwd (gain_q, bias_q,
+ * gain_k, bias_k gradients), all written. out and lse as dilated_attn_fwd_qknorm
+ * returned them. The gain and bias gradients are summed in a fixed order
+ * (no atomics). Other arguments, checks and rules as dilated_attn_bwd; dparams
+ * must not overlap any other buffer (DA_ERR_ALIAS). */
+int dilated_attn_bwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
+                            const void* bias_q, const void* gain_k, const void* bias_k,
+                            float eps, const void* out, const float* lse, const void* dout,
+                            void* dxq, void* dxk, void* dv, float* dparams, int64_t B, int64_t N,
+                            int32_t H, int32_t Dh, const da_pattern* patterns,
+                            int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Test hook: the gather map the kernels use, written by a device kernel
  * through the same index function as the attention kernel.
  * dev_out: device int64 [N / min(w, N)][ceil(min(w, N) / r)], segment-major;

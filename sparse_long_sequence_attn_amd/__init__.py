@@ -18,7 +18,8 @@ __all__ = [
     "coverage_map", "workspace_bytes", "strerror", "version", "load_library", "DilatedAttnError",
     "DA_F32", "DA_BF16", "DA_HEAD_DIM", "DA_MAX_PATTERNS", "Problem", "dilated_attn_bwd",
     "BwdProblem", "bwd_workspace_bytes", "DA_BWD_PREP", "DA_BWD_KV", "DA_BWD_Q", "DA_BWD_MERGE",
-    "DA_BWD_ALL", "qk_norm_fwd", "qk_norm_bwd",
+    "DA_BWD_ALL", "qk_norm_fwd", "qk_norm_bwd", "qknorm_fused_supported", "dilated_attn_qknorm",
+    "dilated_attn_qknorm_bwd",
 ]
 
 
@@ -248,3 +249,108 @@ def qk_norm_bwd(xq, xk, dyq, dyk, gain_q, gain_k, eps=1e-5):
         torch.cuda.current_stream(xq.device).cuda_stream)
     _native.check(code, "dilated_attn_qk_norm_bwd")
     return dxq, dxk, dparams
+
+
+def qknorm_fused_supported(B, N, H, patterns, dtype_code):
+    """True when dilated_attn_qknorm serves this shape and pattern list (one
+    pattern whose segments gather at most 32 rows); asks the library."""
+    try:
+        _native.bwd_qknorm_workspace_bytes(int(B), int(N), int(H), DA_HEAD_DIM,
+                                           [(int(w), int(r)) for (w, r) in patterns],
+                                           int(dtype_code))
+    except DilatedAttnError as e:
+        if e.code == -3:  # DA_ERR_PATTERN
+            return False
+        raise
+    return True
+
+
+def _check_out(name, t, shape, dtype, device):
+    import torch
+
+    if (not isinstance(t, torch.Tensor) or tuple(t.shape) != tuple(shape) or t.dtype != dtype
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+
+
+def _check_fused(xq, xk, v, params):
+    import torch
+
+    for name, t in (("xq", xq), ("xk", xk), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor; no CPU path exists")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, N, H, Dh] tensor")
+        if t.shape != xq.shape or t.dtype != xq.dtype or t.device != xq.device:
+            raise ValueError(f"{name} must match xq in shape, dtype and device")
+    for name, t in zip(("gain_q", "bias_q", "gain_k", "bias_k"), params):
+        _check_rows(name, t, xq)
+        if t.numel() != DA_HEAD_DIM:
+            raise ValueError(f"{name} must hold {DA_HEAD_DIM} values")
+
+
+def dilated_attn_qknorm(xq, xk, v, gain_q, bias_q, gain_k, bias_k, patterns, eps=1e-5,
+                        causal=True, scale=None, out=None, lse=None):
+    """Forward of attention over qk_norm(xq), qk_norm(xk), v with the layer
+    norm applied inside the attention kernel. Returns (out, lse); one pattern
+    with segments of at most 32 gathered rows (see qknorm_fused_supported)."""
+    import torch
+
+    params = (gain_q, bias_q, gain_k, bias_k)
+    _check_fused(xq, xk, v, params)
+    B, N, H, Dh = (int(x) for x in xq.shape)
+    pats = [(int(w), int(r)) for (w, r) in patterns]
+    out = torch.empty_like(xq) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=xq.device) if lse is None else lse
+    _check_out("out", out, xq.shape, xq.dtype, xq.device)
+    _check_out("lse", lse, (B, H, N), torch.float32, xq.device)
+    code = load_library().dilated_attn_fwd_qknorm(
+        xq.data_ptr(), xk.data_ptr(), v.data_ptr(), *(t.data_ptr() for t in params), float(eps),
+        out.data_ptr(), lse.data_ptr(), B, N, H, Dh, _native.pattern_array(pats), len(pats),
+        1 if causal else 0, _dtype_code(xq), float(scale) if scale else 0.0,
+        torch.cuda.current_stream(xq.device).cuda_stream)
+    _native.check(code, "dilated_attn_fwd_qknorm")
+    return out, lse
+
+
+def dilated_attn_qknorm_bwd(xq, xk, v, gain_q, bias_q, gain_k, bias_k, out, lse, dout, patterns,
+                            eps=1e-5, causal=True, scale=None, workspace=None, dxq=None,
+                            dxk=None, dv=None, dparams=None):
+    """Backward of dilated_attn_qknorm. Returns (dxq, dxk, dv, dparams), with
+    dparams a float32 [2, 2, 64] tensor: [q|k][gain|bias]; outputs are
+    allocated unless given."""
+    import torch
+
+    params = (gain_q, bias_q, gain_k, bias_k)
+    _check_fused(xq, xk, v, params)
+    for name, t in (("out", out), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.shape != xq.shape or t.dtype != xq.dtype \
+                or t.device != xq.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like xq")
+    B, N, H, Dh = (int(x) for x in xq.shape)
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, N) or lse.dtype != torch.float32
+            or not lse.is_contiguous() or lse.device != xq.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on xq's device")
+    pats = [(int(w), int(r)) for (w, r) in patterns]
+    dt = _dtype_code(xq)
+    if workspace is None:
+        ws = _native.bwd_qknorm_workspace_bytes(B, N, H, Dh, pats, dt)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=xq.device)
+    dxq = torch.empty_like(xq) if dxq is None else dxq
+    dxk = torch.empty_like(xk) if dxk is None else dxk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dparams is None:
+        dparams = torch.empty((2, 2, DA_HEAD_DIM), dtype=torch.float32, device=xq.device)
+    for name, t in (("dxq", dxq), ("dxk", dxk), ("dv", dv)):
+        _check_out(name, t, xq.shape, xq.dtype, xq.device)
+    _check_out("dparams", dparams, (2, 2, DA_HEAD_DIM), torch.float32, xq.device)
+    code = load_library().dilated_attn_bwd_qknorm(
+        xq.data_ptr(), xk.data_ptr(), v.data_ptr(), *(t.data_ptr() for t in params), float(eps),
+        out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dxq.data_ptr(), dxk.data_ptr(),
+        dv.data_ptr(), dparams.data_ptr(), B, N, H, Dh, _native.pattern_array(pats), len(pats),
+        1 if causal else 0, dt, float(scale) if scale else 0.0, workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(),
+        torch.cuda.current_stream(xq.device).cuda_stream)
+    _native.check(code, "dilated_attn_bwd_qknorm")
+    return dxq, dxk, dv, dparams

@@ -198,8 +198,10 @@ int check_buffers(const Plan& pl, const void* q, const void* k, const void* v, c
   return DA_OK;
 }
 
+// qkn: gain_q, bias_q, gain_k, bias_k of the fused qk_norm, or null
 int run_attention(const Plan& pl, const void* q, const void* k, const void* v, void* out,
-                  float* lse, void* ws, hipStream_t st) {
+                  float* lse, void* ws, hipStream_t st, const void* const* qkn = nullptr,
+                  float qkn_eps = 0.f) {
   da::AttnArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;
@@ -214,8 +216,14 @@ int run_attention(const Plan& pl, const void* q, const void* k, const void* v, v
   a.np = pl.np;
   a.sl2 = pl.sl2;
   sorted_patterns(pl, pl.fwd, a.pat, a.unit_start);
-  const hipError_t e =
-      da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.fwd.grid, st);
+  hipError_t e;
+  if (qkn) {
+    for (int i = 0; i < 4; ++i) a.qkn[i] = qkn[i];
+    a.qkn_eps = qkn_eps;
+    e = da::launch_attention_qkn(a, pl.bf16, pl.causal, pl.fwd.grid, st);
+  } else {
+    e = da::launch_attention(a, pl.bf16, pl.nw, pl.causal, pl.np == 1, pl.fwd.grid, st);
+  }
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
@@ -281,16 +289,73 @@ int check_bwd_buffers(const Plan& pl, const void* q, const void* k, const void* 
   return DA_OK;
 }
 
+// The fused form serves one pattern whose segments gather at most 32 rows
+// (the plan's one-wave case), where every output row is final.
+int qkn_params_check(const Plan& pl, const void* const* gb, float eps, const void* const* outs,
+                     const size_t* out_bytes, int n_outs) {
+  if (!isfinite(eps) || !(eps > 0.f)) return DA_ERR_ARG;
+  if (pl.empty) return DA_OK;
+  if (pl.np != 1 || pl.nw != 1) return DA_ERR_PATTERN;
+  const size_t pb = (size_t)DA_HEAD_DIM * (pl.bf16 ? 2 : 4);
+  for (int i = 0; i < 4; ++i) {
+    if (!gb[i]) return DA_ERR_NULL;
+    if (((uintptr_t)gb[i] & 15) != 0) return DA_ERR_ALIGN;
+    for (int j = 0; j < n_outs; ++j)
+      if (overlaps(outs[j], out_bytes[j], gb[i], pb)) return DA_ERR_ALIAS;
+  }
+  return DA_OK;
+}
+
+// Workspace of the fused qk_norm backward: the plain backward's, then the
+// per-unit gain/bias partials [2][units][2 kDh], then their folded form
+// [2][groups][2 kDh] (floats, 256-byte aligned regions).
+size_t qkn_part_offset(const Plan& pl) { return (pl.bwd_ws_bytes + 255) & ~(size_t)255; }
+size_t qkn_fold_offset(const Plan& pl) {
+  const size_t part = (size_t)2 * pl.pat[0].units * 2 * DA_HEAD_DIM * 4;
+  return (qkn_part_offset(pl) + part + 255) & ~(size_t)255;
+}
+size_t qkn_bwd_ws_bytes(const Plan& pl) {
+  return qkn_fold_offset(pl) + (size_t)2 * da::qkn_groups(pl.pat[0].units) * 2 * DA_HEAD_DIM * 4;
+}
+
+// qkn (gain_q, bias_q, gain_k, bias_k) and dparams are set for the fused
+// qk_norm backward (checked by the caller), null otherwise.
 int bwd_common(int stages, const void* q, const void* k, const void* v, const void* out,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
                int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
                int32_t causal, int32_t dtype, float scale, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, void* stream, const void* const* qkn = nullptr,
+               float qkn_eps = 0.f, float* dparams = nullptr) {
   if (stages < 1 || stages > DA_BWD_ALL) return DA_ERR_ARG;
   Plan pl;
   int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
-  if (rc != DA_OK || pl.empty) return rc;
-  rc = check_bwd_buffers(pl, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes);
+  if (rc != DA_OK) return rc;
+  if (qkn) {
+    const void* outs[4] = {dq, dk, dv, dparams};
+    const size_t ob[4] = {pl.tensor_bytes, pl.tensor_bytes, pl.tensor_bytes,
+                          (size_t)4 * DA_HEAD_DIM * 4};
+    rc = qkn_params_check(pl, qkn, qkn_eps, outs, ob, 4);
+    if (rc != DA_OK || pl.empty) return rc;
+    const void* wsv[1] = {workspace};
+    const size_t wsb[1] = {qkn_bwd_ws_bytes(pl)};
+    rc = qkn_params_check(pl, qkn, qkn_eps, wsv, wsb, 1);
+    if (rc != DA_OK) return rc;
+    if (!dparams) return DA_ERR_NULL;
+    if (((uintptr_t)dparams & 3) != 0) return DA_ERR_ALIGN;
+    const size_t pb = (size_t)4 * DA_HEAD_DIM * 4;
+    const void* ins[6] = {q, k, v, out, dout, lse};
+    const size_t isz[6] = {pl.tensor_bytes, pl.tensor_bytes, pl.tensor_bytes, pl.tensor_bytes,
+                           pl.tensor_bytes, pl.lse_bytes};
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(dparams, pb, ins[j], isz[j])) return DA_ERR_ALIAS;
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(dparams, pb, outs[j], pl.tensor_bytes)) return DA_ERR_ALIAS;
+    if (overlaps(dparams, pb, workspace, qkn_bwd_ws_bytes(pl))) return DA_ERR_ALIAS;
+  }
+  if (pl.empty) return DA_OK;
+  Plan chk = pl;  // the fused qk_norm backward needs room for its partials
+  if (qkn) chk.bwd_ws_bytes = qkn_bwd_ws_bytes(pl);
+  rc = check_bwd_buffers(chk, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes);
   if (rc != DA_OK) return rc;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* ws = reinterpret_cast<float*>(workspace);
@@ -334,6 +399,14 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   a.scale = pl.scale;
   sorted_patterns(pl, pl.bwd, a.pat, a.unit_start);
   for (int j = 0; j < pl.np; ++j) a.pat[j].po_off = pl.bwd_po_off[pl.bwd.order[j]];
+  float* const qkn_part =
+      reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + qkn_part_offset(pl));
+  if (qkn) {
+    for (int i = 0; i < 4; ++i) a.qkn[i] = qkn[i];
+    a.qkn_eps = qkn_eps;
+    a.qkn_part = qkn_part;
+    a.qkn_units = pl.pat[0].units;
+  }
 
   hipError_t e = hipSuccess;
   // every segment at most 32 rows: one kernel (in the KV stage) computes D,
@@ -346,6 +419,13 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   if (e == hipSuccess && !fused && (stages & DA_BWD_Q))
     e = da::launch_bwd_q(a, pl.bf16, pl.causal, pl.bwd.grid, st);
   if (e == hipSuccess && (stages & DA_BWD_MERGE)) e = da::launch_bwd_merge(ra, pl.bf16, st);
+  if (e == hipSuccess && qkn && (stages & DA_BWD_MERGE)) {
+    float* const folded =
+        reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + qkn_fold_offset(pl));
+    e = da::launch_qkn_fold(qkn_part, pl.pat[0].units, folded, st);
+    if (e == hipSuccess)
+      e = da::launch_qk_norm_reduce(folded, da::qkn_groups(pl.pat[0].units), dparams, st);
+  }
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
@@ -398,6 +478,54 @@ int dilated_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
                      void* workspace, size_t workspace_bytes, void* stream) {
   return fwd_common(kBoth, q, k, v, out, lse, B, N, H, Dh, patterns, n_patterns, causal, dtype,
                     scale, workspace, workspace_bytes, stream);
+}
+
+int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
+                            const void* bias_q, const void* gain_k, const void* bias_k,
+                            float eps, void* out, float* lse, int64_t B, int64_t N, int32_t H,
+                            int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
+                            int32_t causal, int32_t dtype, float scale, void* stream) {
+  Plan pl;
+  int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
+  if (rc != DA_OK) return rc;
+  const void* gb[4] = {gain_q, bias_q, gain_k, bias_k};
+  const void* outs[2] = {out, lse};
+  const size_t ob[2] = {pl.tensor_bytes, pl.lse_bytes};
+  rc = qkn_params_check(pl, gb, eps, outs, ob, 2);
+  if (rc != DA_OK || pl.empty) return rc;
+  rc = check_buffers(pl, xq, xk, v, out, lse, nullptr, 0);
+  if (rc != DA_OK) return rc;
+  return run_attention(pl, xq, xk, v, out, lse, nullptr, reinterpret_cast<hipStream_t>(stream),
+                       gb, eps);
+}
+
+int dilated_attn_bwd_qknorm_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
+                                            const da_pattern* patterns, int32_t n_patterns,
+                                            int32_t dtype, size_t* bytes) {
+  if (!bytes) return DA_ERR_NULL;
+  Plan pl;
+  const int rc = make_plan(B, N, H, Dh, patterns, n_patterns, 1, dtype, 0.f, &pl);
+  if (rc != DA_OK) return rc;
+  if (pl.empty) {
+    *bytes = 0;
+    return DA_OK;
+  }
+  if (pl.np != 1 || pl.nw != 1) return DA_ERR_PATTERN;
+  *bytes = qkn_bwd_ws_bytes(pl);
+  return DA_OK;
+}
+
+int dilated_attn_bwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
+                            const void* bias_q, const void* gain_k, const void* bias_k,
+                            float eps, const void* out, const float* lse, const void* dout,
+                            void* dxq, void* dxk, void* dv, float* dparams, int64_t B, int64_t N,
+                            int32_t H, int32_t Dh, const da_pattern* patterns,
+                            int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  const void* gb[4] = {gain_q, bias_q, gain_k, bias_k};
+  return bwd_common(DA_BWD_ALL, xq, xk, v, out, lse, dout, dxq, dxk, dv, B, N, H, Dh, patterns,
+                    n_patterns, causal, dtype, scale, workspace, workspace_bytes, stream, gb, eps,
+                    dparams);
 }
 
 int dilated_attn_fwd_attention(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -32,6 +32,14 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair, round to nearest even (the hardware convert)
+__device__ inline uint32_t pack_bf16_rne(float x, float y) {
+  bf16x2 p;
+  p[0] = (__bf16)x;
+  p[1] = (__bf16)y;
+  return __builtin_bit_cast(uint32_t, p);
+}
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -135,9 +143,12 @@ struct Smem {
 // K and V fragment read from LDS feeds QB MFMAs); BN keys per LDS tile.
 // 4 waves per SIMD: the bf16 4-wave configuration fits in 128 VGPRs without
 // spills (configurations that do not fit keep their natural allocation).
-template <int NW, int QB, int BN, bool CAUSAL, bool FINAL, bool BF>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
-attn_fwd_kernel(const AttnArgs a) {
+// QKN: the DilatedAttention module's qk_norm applied to q and k as they are
+// loaded (one-wave workgroups only): each 64-value row becomes
+// (x - mean) / sqrt(var + eps) * gain + bias, statistics in fp32.
+template <int NW, int QB, int BN, bool CAUSAL, bool FINAL, bool BF, bool QKN = false>
+__global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const AttnArgs a) {
+  static_assert(!QKN || (NW == 1 && QB == 1), "qk_norm is fused into one-wave workgroups only");
   using T = typename std::conditional<BF, __bf16, float>::type;
   // one-wave workgroups serve segments of at most 32 gathered rows (one key
   // tile): a single LDS buffer, so more workgroups fit on a CU
@@ -223,6 +234,60 @@ attn_fwd_kernel(const AttnArgs a) {
     }
   }
 
+  if constexpr (QKN) {
+    // this lane holds 32 of the row's 64 values, the lane 32 apart the rest
+    // (bf16: dims 16 ks + 8 hh + e; fp32: dims 4 c + hh and 4 c + 2 + hh)
+    float x[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if constexpr (BF) {
+        const uint32_t w = __builtin_bit_cast(u32x4, qf[0][i / 8])[(i % 8) / 2];
+        x[i] = __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+      } else {
+        x[i] = qf[0][i];
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s += x[i];
+    const float mu = pair_sum(s) * (1.f / kDh);
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v = fmaf(x[i] - mu, x[i] - mu, v);
+    const float rstd = __builtin_amdgcn_rsqf(pair_sum(v) * (1.f / kDh) + a.qkn_eps);
+    if constexpr (BF) {
+      const __bf16* gq = reinterpret_cast<const __bf16*>(a.qkn[0]) + 8 * hh;
+      const __bf16* bq = reinterpret_cast<const __bf16*>(a.qkn[1]) + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 gw = *reinterpret_cast<const u32x4*>(gq + 16 * ks);
+        const u32x4 bw = *reinterpret_cast<const u32x4*>(bq + 16 * ks);
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y0 = fmaf((x[8 * ks + 2 * j] - mu) * rstd, __uint_as_float(gw[j] << 16),
+                                __uint_as_float(bw[j] << 16));
+          const float y1 = fmaf((x[8 * ks + 2 * j + 1] - mu) * rstd,
+                                __uint_as_float(gw[j] & 0xffff0000u),
+                                __uint_as_float(bw[j] & 0xffff0000u));
+          o[j] = pack_bf16_rne(y0, y1);
+        }
+        qf[0][ks] = __builtin_bit_cast(bf16x8, o);
+      }
+    } else {
+      const float* gq = reinterpret_cast<const float*>(a.qkn[0]);
+      const float* bq = reinterpret_cast<const float*>(a.qkn[1]);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const f32x4 gw = *reinterpret_cast<const f32x4*>(gq + 4 * c);
+        const f32x4 bw = *reinterpret_cast<const f32x4*>(bq + 4 * c);
+        qf[0][2 * c] = fmaf((x[2 * c] - mu) * rstd, hh ? gw[1] : gw[0], hh ? bw[1] : bw[0]);
+        qf[0][2 * c + 1] =
+            fmaf((x[2 * c + 1] - mu) * rstd, hh ? gw[3] : gw[2], hh ? bw[3] : bw[2]);
+      }
+    }
+  }
+
   // ---- key/value tile staging: global -> registers -> LDS. Thread chunk c
   // of a tile is 16 bytes of row c / (row bytes / 16); K and V share offsets.
   constexpr int kChunksPerRow = kRowBytes / 16;  // 8 (bf16) or 16 (fp32)
@@ -252,6 +317,48 @@ attn_fwd_kernel(const AttnArgs a) {
   auto store_tile = [&](int buf) {
     T* K = Ks + buf * SM::kKElems;
     T* V = Vs + buf * SM::kVElems;
+    if constexpr (QKN) {
+      // each row's chunks sit in kChunksPerRow consecutive lanes (c % chunks
+      // = tid % chunks, since NT is a multiple): statistics over those lanes
+      const T* gk = reinterpret_cast<const T*>(a.qkn[2]);
+      const T* bk = reinterpret_cast<const T*>(a.qkn[3]);
+      constexpr int VPC = BF ? 8 : 4;  // values per chunk
+      const int d0 = (tid % kChunksPerRow) * VPC;
+#pragma unroll
+      for (int i = 0; i < CK; ++i) {
+        float x[VPC];
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) {
+          if constexpr (BF)
+            x[e] = __uint_as_float((e & 1) ? (kreg[i][e / 2] & 0xffff0000u) : (kreg[i][e / 2] << 16));
+          else
+            x[e] = __uint_as_float(kreg[i][e]);
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) s += x[e];
+#pragma unroll
+        for (int m = 1; m < kChunksPerRow; m *= 2) s += __shfl_xor(s, m);
+        const float mu = s * (1.f / kDh);
+        float v = 0.f;
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) v = fmaf(x[e] - mu, x[e] - mu, v);
+#pragma unroll
+        for (int m = 1; m < kChunksPerRow; m *= 2) v += __shfl_xor(v, m);
+        const float rstd = __builtin_amdgcn_rsqf(v * (1.f / kDh) + a.qkn_eps);
+#pragma unroll
+        for (int e = 0; e < VPC; ++e)
+          x[e] = fmaf((x[e] - mu) * rstd, (float)gk[d0 + e], (float)bk[d0 + e]);
+#pragma unroll
+        for (int e = 0; e < VPC; ++e) {
+          if constexpr (BF) {
+            if (e & 1) kreg[i][e / 2] = pack_bf16_rne(x[e - 1], x[e]);
+          } else {
+            kreg[i][e] = __float_as_uint(x[e]);
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
       const int c = tid + i * NT;
@@ -700,6 +807,23 @@ constexpr int kQbBf16 = 1;
 }  // namespace
 
 int attn_tile_rows(bool bf16, int nw) { return nw == 4 ? 32 * nw * (bf16 ? kQbBf16 : 1) : 32; }
+
+hipError_t launch_attention_qkn(const AttnArgs& a, bool bf16, bool causal, int64_t grid,
+                                hipStream_t st) {
+  const dim3 g((uint32_t)grid), b(64);
+  if (bf16) {
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_kernel<1, 1, 32, true, true, true, true>), g, b, 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<1, 1, 32, false, true, true, true>), g, b, 0, st, a);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((attn_fwd_kernel<1, 1, 32, true, true, false, true>), g, b, 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<1, 1, 32, false, true, false, true>), g, b, 0, st, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, bool final_out,
                             int64_t grid, hipStream_t st) {

@@ -670,6 +670,155 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- qk_norm helpers
+
+// Layer norm of the staged rows of one tensor in registers (chunk i of this
+// lane: row (lane + 64 i) / CPR, chunk lane % CPR; a row's chunks sit in CPR
+// consecutive lanes): (x - mean) / sqrt(var + eps) * gain + bias, statistics
+// in fp32 over the row's 64 values. The lane holding chunk 0 of a row
+// records its mean and rstd. Rows from L on (past the segment's gathered
+// rows) stay zero, as the unnormalised path leaves them.
+template <bool BF, int CK>
+__device__ inline void qkn_normalize(u32x4 (&r)[CK], const void* gain, const void* bias,
+                                     float eps, int L, int lane, float* mean_out,
+                                     float* rstd_out) {
+  constexpr int CPR = BF ? 8 : 16;  // chunks per row
+  constexpr int VPC = BF ? 8 : 4;   // values per chunk
+  const int d0 = (lane % CPR) * VPC;
+  float gv[VPC], bv[VPC];
+#pragma unroll
+  for (int e = 0; e < VPC; ++e) {
+    if constexpr (BF) {
+      gv[e] = (float)reinterpret_cast<const __bf16*>(gain)[d0 + e];
+      bv[e] = (float)reinterpret_cast<const __bf16*>(bias)[d0 + e];
+    } else {
+      gv[e] = reinterpret_cast<const float*>(gain)[d0 + e];
+      bv[e] = reinterpret_cast<const float*>(bias)[d0 + e];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CK; ++i) {
+    float x[VPC];
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) {
+      if constexpr (BF)
+        x[e] = __uint_as_float((e & 1) ? (r[i][e / 2] & 0xffff0000u) : (r[i][e / 2] << 16));
+      else
+        x[e] = __uint_as_float(r[i][e]);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) s += x[e];
+#pragma unroll
+    for (int m = 1; m < CPR; m *= 2) s += __shfl_xor(s, m);
+    const float mu = s * (1.f / kDh);
+    float v = 0.f;
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) v = fmaf(x[e] - mu, x[e] - mu, v);
+#pragma unroll
+    for (int m = 1; m < CPR; m *= 2) v += __shfl_xor(v, m);
+    const float rstd = __builtin_amdgcn_rsqf(v * (1.f / kDh) + eps);
+    const int row = (lane + 64 * i) / CPR;
+    if (lane % CPR == 0) {
+      mean_out[row] = mu;
+      rstd_out[row] = rstd;
+    }
+    const float keep = row < L ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) x[e] = fmaf((x[e] - mu) * rstd, gv[e], bv[e]) * keep;
+#pragma unroll
+    for (int e = 0; e < VPC; ++e) {
+      if constexpr (BF) {
+        if (e & 1) r[i][e / 2] = dev_pack_bf16(x[e - 1], x[e]);
+      } else {
+        r[i][e] = __float_as_uint(x[e]);
+      }
+    }
+  }
+}
+
+// write_rows for a tensor that went through the fused qk_norm: the staged
+// rows are the gradient dy with respect to the normalised rows; with
+// g = dy * gain and xh = (x - mean) * rstd (x re-read from global memory)
+// each final row becomes dx = rstd * (g - mean(g) - xh * mean(g * xh)).
+// The lane's 4 columns of dy * xh and dy are summed over the rows it writes
+// and then over the wave into part[0 .. 2 kDh) (gain, then bias).
+template <bool BF>
+__device__ inline void write_rows_qkn(const float* srow, const int32_t* mpos,
+                                      const int32_t* mkind, void* final_base, int64_t rs,
+                                      __amdgpu_buffer_rsrc_t rx, uint32_t mbytes,
+                                      const float* mean, const float* rstd, const void* gain,
+                                      float* part, int lane) {
+  using T = typename std::conditional<BF, __bf16, float>::type;
+  const int sr = lane >> 4, sc = lane & 15;
+  float gn[4], acc_g[4] = {0.f, 0.f, 0.f, 0.f}, acc_b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) gn[e] = (float)reinterpret_cast<const T*>(gain)[4 * sc + e];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int R = 4 * i + sr;
+    const bool live = mkind[R] == 1;  // uniform over the row's 16 lanes
+    const f32x4 dy = *reinterpret_cast<const f32x4*>(srow + R * kStageStride + 4 * sc);
+    float x[4];
+    if constexpr (BF) {
+      const u32x2 w = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)R * mbytes + 8 * sc, 0, 0));
+      x[0] = __uint_as_float(w[0] << 16);
+      x[1] = __uint_as_float(w[0] & 0xffff0000u);
+      x[2] = __uint_as_float(w[1] << 16);
+      x[3] = __uint_as_float(w[1] & 0xffff0000u);
+    } else {
+      const f32x4 w = __builtin_bit_cast(f32x4, dev_load16(rx, (uint32_t)R * mbytes + 16 * sc));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = w[e];
+    }
+    const float mu = mean[R], rs_ = rstd[R];
+    float xh[4], gg[4], sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xh[e] = (x[e] - mu) * rs_;
+      gg[e] = dy[e] * gn[e];
+      sg += gg[e];
+      sgx = fmaf(gg[e], xh[e], sgx);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m *= 2) {
+      sg += __shfl_xor(sg, m);
+      sgx += __shfl_xor(sgx, m);
+    }
+    const float mg = sg * (1.f / kDh), mgx = sgx * (1.f / kDh);
+    float dx[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dx[e] = rs_ * (gg[e] - mg - xh[e] * mgx);
+    if (live) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc_g[e] = fmaf(dy[e], xh[e], acc_g[e]);
+        acc_b[e] += dy[e];
+      }
+      T* dst = reinterpret_cast<T*>(final_base) + (int64_t)mpos[R] * rs + 4 * sc;
+      if constexpr (BF)
+        *reinterpret_cast<u32x2*>(dst) =
+            u32x2{dev_pack_bf16(dx[0], dx[1]), dev_pack_bf16(dx[2], dx[3])};
+      else
+        *reinterpret_cast<f32x4*>(dst) = f32x4{dx[0], dx[1], dx[2], dx[3]};
+    }
+  }
+  // the 4 row groups of the wave hold the same columns: fixed-order sum
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc_g[e] += __shfl_xor(acc_g[e], 16);
+    acc_g[e] += __shfl_xor(acc_g[e], 32);
+    acc_b[e] += __shfl_xor(acc_b[e], 16);
+    acc_b[e] += __shfl_xor(acc_b[e], 32);
+  }
+  if (sr == 0) {
+    *reinterpret_cast<f32x4*>(part + 4 * sc) = f32x4{acc_g[0], acc_g[1], acc_g[2], acc_g[3]};
+    *reinterpret_cast<f32x4*>(part + kDh + 4 * sc) =
+        f32x4{acc_b[0], acc_b[1], acc_b[2], acc_b[3]};
+  }
+}
+
 // ---------------------------------------------------------------- short segments
 
 // Segments of at most 32 gathered rows: one wave takes a whole unit, every
@@ -680,12 +829,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
 // written to LDS, and dQ^T = K^T dS^T takes both operands from transpose
 // reads (K^T of the staged K, dS of the staged dS^T). Rows are written
 // through the LDS staging area as 128-byte lines.
-template <bool CAUSAL, bool BF>
+// QKN: the module's qk_norm fused in (a.qkn set; one pattern): q and k rows
+// are normalised while staged, and the dq, dk rows go through the layer
+// norm's backward before they are written.
+template <bool CAUSAL, bool BF, bool QKN = false>
 __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
   using T = typename std::conditional<BF, __bf16, float>::type;
   constexpr int ST = lds_stride<BF>();
   constexpr int kTileBytes = 32 * ST * (int)sizeof(T);
-  constexpr int kBytes = 3 * kTileBytes + 2 * 32 * 4;  // Q, dout then dS^T, K; lse2, D
+  // Q, dout then dS^T, K; lse2, D; qk_norm row statistics (q mean, q rstd,
+  // k mean, k rstd)
+  constexpr int kBytes = 3 * kTileBytes + 2 * 32 * 4 + (QKN ? 4 * 32 * 4 : 0);
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
   static_assert(3 * kTileBytes >= kStageBytes, "epilogue staging fits the tiles");
   __shared__ __attribute__((aligned(16))) char smem[kBytes];
@@ -694,6 +848,7 @@ __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
   T* const Ks = reinterpret_cast<T*>(smem + 2 * kTileBytes);
   float* const ls = reinterpret_cast<float*>(smem + 3 * kTileBytes);
   float* const dd = ls + 32;
+  float* const qst = dd + 32;  // qk_norm statistics (QKN only)
 
   UnitTile tl;
   if (!decode_unit_tile<false>(a, blockIdx.x, &tl)) return;
@@ -743,6 +898,10 @@ __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
 #pragma unroll
     for (int m = 1; m < CPR; m *= 2) s += __shfl_xor(s, m);
     if (lane % CPR == 0) dd[(lane + 64 * i) / CPR] = s;
+  }
+  if constexpr (QKN) {
+    qkn_normalize<BF>(sqd.ra, a.qkn[0], a.qkn[1], a.qkn_eps, g.L, lane, qst, qst + 32);
+    qkn_normalize<BF>(sko.ra, a.qkn[2], a.qkn[3], a.qkn_eps, g.L, lane, qst + 64, qst + 96);
   }
   sqd.store(lane, Qs, Ds);
   sko.store_first(lane, Ks);
@@ -876,12 +1035,25 @@ __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
   float* const part = a.ws + P.po_off + prow0 * kDh;
   stage_row(srow, dQ, a.scale, n, hh);
   __syncthreads();
-  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, part, lane);
+  if constexpr (QKN) {
+    const int64_t unit = prow0 / P.lmax;
+    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, rq,
+                       g.mbytes, qst, qst + 32, a.qkn[0], a.qkn_part + unit * 2 * kDh, lane);
+  } else {
+    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, part, lane);
+  }
   __syncthreads();
   stage_row(srow, dK, a.scale, n, hh);
   __syncthreads();
-  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs,
-                 part + slots * kDh, lane);
+  if constexpr (QKN) {
+    const int64_t unit = prow0 / P.lmax;
+    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs, rk,
+                       g.mbytes, qst + 64, qst + 96, a.qkn[2],
+                       a.qkn_part + (a.qkn_units + unit) * 2 * kDh, lane);
+  } else {
+    write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs,
+                   part + slots * kDh, lane);
+  }
   __syncthreads();
   stage_row(srow, dV, 1.f, n, hh);
   __syncthreads();
@@ -1038,11 +1210,33 @@ hipError_t launch_q_cfg(const BwdArgs& a, bool causal, int64_t grid, hipStream_t
 template <bool BF>
 hipError_t launch_short_cfg(const BwdArgs& a, bool causal, int64_t grid, hipStream_t st) {
   const dim3 g((uint32_t)grid), b(64);
-  if (causal)
+  if (a.qkn[0]) {
+    if (causal)
+      hipLaunchKernelGGL((bwd_short_kernel<true, BF, true>), g, b, 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_short_kernel<false, BF, true>), g, b, 0, st, a);
+  } else if (causal) {
     hipLaunchKernelGGL((bwd_short_kernel<true, BF>), g, b, 0, st, a);
-  else
+  } else {
     hipLaunchKernelGGL((bwd_short_kernel<false, BF>), g, b, 0, st, a);
+  }
   return hipGetLastError();
+}
+
+// out[w][grp][c] = sum over units u of group grp (consecutive, in order) of
+// in[w][u][c]: the per-unit qk_norm gradient partials folded into at most
+// kQknGroups rows per tensor; one block per (group, tensor), a thread per
+// column, so every read is a contiguous row.
+constexpr int kQknGroups = 1024;
+__global__ __launch_bounds__(2 * kDh) void qkn_fold_kernel(const float* in, int64_t units,
+                                                           int64_t per_group, int64_t groups,
+                                                           float* out) {
+  const int64_t grp = blockIdx.x, w = blockIdx.y;
+  const int c = threadIdx.x;
+  const int64_t u0 = grp * per_group, u1 = min(units, u0 + per_group);
+  float s = 0.f;
+  for (int64_t u = u0; u < u1; ++u) s += in[(w * units + u) * 2 * kDh + c];
+  out[(w * groups + grp) * 2 * kDh + c] = s;
 }
 
 dim3 row_grid(const BwdRowArgs& a) {
@@ -1078,6 +1272,16 @@ hipError_t launch_bwd_kv(const BwdArgs& a, bool bf16, bool causal, int64_t grid,
 hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, bool causal, int64_t grid, hipStream_t st) {
   return bf16 ? launch_q_cfg<4, true>(a, causal, grid, st)
               : launch_q_cfg<4, false>(a, causal, grid, st);
+}
+
+int64_t qkn_groups(int64_t units) { return units < kQknGroups ? units : kQknGroups; }
+
+hipError_t launch_qkn_fold(const float* part, int64_t units, float* folded, hipStream_t st) {
+  const int64_t groups = qkn_groups(units);
+  const int64_t per = (units + groups - 1) / groups;
+  hipLaunchKernelGGL(qkn_fold_kernel, dim3((uint32_t)groups, 2), dim3(2 * kDh), 0, st, part,
+                     units, per, groups, folded);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_short(const BwdArgs& a, bool bf16, bool causal, int64_t grid,

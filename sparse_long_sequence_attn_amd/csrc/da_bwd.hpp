@@ -33,6 +33,14 @@ struct BwdArgs {
   int32_t np;
   float sl2;    // softmax scale * log2(e)
   float scale;  // softmax scale
+  // qk_norm fused into the short-segment kernel: gain_q, bias_q, gain_k,
+  // bias_k (q's dtype), or null; q and k then hold the un-normalised rows
+  // and dq, dk receive their gradients. qkn_part: [2 (q, k)][qkn_units][2 *
+  // kDh] per-unit partial sums of the gain and bias gradients.
+  const void* qkn[4];
+  float qkn_eps;
+  float* qkn_part;
+  int64_t qkn_units;
   PatDev pat[kMaxPat];
   int64_t unit_start[kMaxPat + 1];
 };

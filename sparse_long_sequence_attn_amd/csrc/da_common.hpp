@@ -77,7 +77,10 @@ struct AttnArgs {
   int32_t H;
   int32_t np;
   float sl2;       // softmax scale * log2(e)
-  int32_t pad_;
+  float qkn_eps;   // qk_norm fused into the loads (one-wave kernel): epsilon
+  // qk_norm fused: gain_q, bias_q, gain_k, bias_k (Dh values each, q's dtype);
+  // q and k then hold the un-normalised rows
+  const void* qkn[4];
   PatDev pat[kMaxPat];
   int64_t unit_start[kMaxPat + 1];  // first global unit of each sorted pattern
 };

@@ -15,6 +15,11 @@ int attn_tile_rows(bool bf16, int nw);
 // LDS tiles) or 1 (32-row tiles, 32-key LDS tiles, for short segments).
 hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, bool final_out,
                             int64_t grid, hipStream_t st);
+// The one-wave attention kernel with the module's qk_norm applied to q and k
+// as they are loaded (a.qkn, a.qkn_eps set; one pattern, segments of at most
+// 32 gathered rows, final outputs).
+hipError_t launch_attention_qkn(const AttnArgs& a, bool bf16, bool causal, int64_t grid,
+                                hipStream_t st);
 
 // Log-sum-exp merge of the per-pattern partials into out and lse.
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st);
@@ -30,6 +35,13 @@ hipError_t launch_bwd_q(const BwdArgs& a, bool bf16, bool causal, int64_t grid, 
 hipError_t launch_bwd_short(const BwdArgs& a, bool bf16, bool causal, int64_t grid,
                             hipStream_t st);
 hipError_t launch_bwd_merge(const BwdRowArgs& a, bool bf16, hipStream_t st);
+// Fused qk_norm backward: the short-segment kernel's per-unit gain/bias
+// gradient partials [2][units][2 kDh] folded (fixed order) into
+// [2][qkn_groups(units)][2 kDh], then summed by launch_qk_norm_reduce.
+int64_t qkn_groups(int64_t units);
+hipError_t launch_qkn_fold(const float* part, int64_t units, float* folded, hipStream_t st);
+hipError_t launch_qk_norm_reduce(const float* partials, int64_t nblk, float* dparams,
+                                 hipStream_t st);
 
 // qk_norm (qknorm_kernel.hip): blocks per tensor for `rows` rows; forward;
 // backward (row gradients, per-block partials of the gain and bias

@@ -16,6 +16,7 @@
 // are reduced without atomics: each lane accumulates its 8 columns over the
 // rows it visits, each block reduces its lanes in LDS into one partial row
 // of 128 floats, and a second kernel adds the partials in a fixed order.
+#include <cstring>
 #include <type_traits>
 
 #include "da_device.hpp"
@@ -231,6 +232,16 @@ hipError_t launch_qk_norm_bwd(const QkNormArgs& a, bool bf16, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(qk_norm_reduce_kernel, dim3(2 * 2 * kDh), dim3(kThreads), 0, st, a, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm_reduce(const float* partials, int64_t nblk, float* dparams,
+                                 hipStream_t st) {
+  QkNormArgs a;
+  memset(&a, 0, sizeof a);
+  a.partials = const_cast<float*>(partials);
+  a.dparams = dparams;
+  hipLaunchKernelGGL(qk_norm_reduce_kernel, dim3(2 * 2 * kDh), dim3(kThreads), 0, st, a, nblk);
   return hipGetLastError();
 }
 

@@ -11,14 +11,20 @@ expansion reaches 1 billion+"), qk_norm layer-normalises each head's query
 and key vectors, the dilated attention runs in this library's kernels, and
 an output projection maps the heads back to dim. The projections are plain
 library GEMMs (torch), with the weight gradients split over the long row
-dimension so that they fill the chip; qk_norm runs in this library's fused
-layer-norm kernels (both tensors in one launch each way).
+dimension so that they fill the chip. qk_norm runs inside the attention
+kernels where the library supports it (one pattern whose segments gather at
+most 32 rows, as in the README's usage example): q and k are normalised as
+the kernels load them and never stored, and the backward kernel turns the
+attention gradients into gradients of the un-normalised rows and of the
+gains and biases. Elsewhere it runs in this library's layer-norm kernels
+(both tensors in one launch each way) before the attention.
 """
 from typing import Optional, Sequence, Tuple, Union
 
 import torch
 
-from . import BwdProblem, Problem, qk_norm_bwd, qk_norm_fwd
+from . import (BwdProblem, Problem, _dtype_code, dilated_attn_qknorm, dilated_attn_qknorm_bwd,
+               qk_norm_bwd, qk_norm_fwd, qknorm_fused_supported)
 
 Pattern = Tuple[int, int]
 
@@ -60,6 +66,28 @@ class QKNormFunction(torch.autograd.Function):
         dxq, dxk, dp = qk_norm_bwd(xq, xk, dyq.contiguous(), dyk.contiguous(), gq, gk, ctx.eps)
         dp = dp.to(gq.dtype)
         return dxq, dxk, dp[0, 0], dp[0, 1], dp[1, 0], dp[1, 1], None
+
+
+class QKNormAttnFunction(torch.autograd.Function):
+    """out = dilated attention(qk_norm(xq), qk_norm(xk), v) with the layer
+    norm inside the attention kernels; the normalised q and k never exist in
+    memory."""
+
+    @staticmethod
+    def forward(ctx, xq, xk, v, gq, bq, gk, bk, eps, patterns, causal, scale):
+        out, lse = dilated_attn_qknorm(xq, xk, v, gq, bq, gk, bk, patterns, eps, causal, scale)
+        ctx.save_for_backward(xq, xk, v, gq, bq, gk, bk, out, lse)
+        ctx.eps, ctx.patterns, ctx.causal, ctx.scale = eps, patterns, causal, scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        xq, xk, v, gq, bq, gk, bk, out, lse = ctx.saved_tensors
+        dxq, dxk, dv, dp = dilated_attn_qknorm_bwd(xq, xk, v, gq, bq, gk, bk, out, lse,
+                                                   dout.contiguous(), ctx.patterns, ctx.eps,
+                                                   ctx.causal, ctx.scale)
+        dp = dp.to(gq.dtype)
+        return (dxq, dxk, dv, dp[0, 0], dp[0, 1], dp[1, 0], dp[1, 1], None, None, None, None)
 
 
 def _weight_grad(dy2, x2):
@@ -160,11 +188,27 @@ class DilatedAttention(torch.nn.Module):
         if self.qk_norm:
             self.q_norm = torch.nn.LayerNorm(self.HEAD_DIM, eps=ln_eps, **f)
             self.k_norm = torch.nn.LayerNorm(self.HEAD_DIM, eps=ln_eps, **f)
+        self.fuse_qk_norm = True  # set False to run qk_norm as separate kernels
+        self._fusable = {}
+
+    def _fused(self, x, B, N):
+        if not (self.qk_norm and self.fuse_qk_norm and self.q_norm.eps == self.k_norm.eps):
+            return False
+        key = (B, N, x.dtype)
+        if key not in self._fusable:
+            self._fusable[key] = qknorm_fused_supported(B, N, self.heads, self.patterns,
+                                                        _dtype_code(x))
+        return self._fusable[key]
 
     def forward(self, x):
         B, N, _ = x.shape
         shape = (B, N, self.heads, self.HEAD_DIM)
         q, k, v = (t.view(shape) for t in _project(x, [self.to_q, self.to_k, self.to_v]))
+        if self._fused(x, B, N):
+            o = QKNormAttnFunction.apply(q, k, v, self.q_norm.weight, self.q_norm.bias,
+                                         self.k_norm.weight, self.k_norm.bias, self.q_norm.eps,
+                                         self.patterns, self.causal, self.scale)
+            return _project(o.view(B, N, self.dim), [self.to_out])[0]
         if self.qk_norm:
             q, k = QKNormFunction.apply(q, k, self.q_norm.weight, self.q_norm.bias,
                                         self.k_norm.weight, self.k_norm.bias, self.q_norm.eps)

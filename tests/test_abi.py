@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_native.SIGNATURES)
@@ -285,3 +285,83 @@ def test_qk_norm_workspace_bytes(lib):
     out = ctypes.c_size_t(0)
     assert lib.dilated_attn_qk_norm_workspace_bytes(-1, ctypes.byref(out)) == -2
     assert lib.dilated_attn_qk_norm_workspace_bytes(5, None) == -1
+
+
+# ---------------------------------------------------------------- qk_norm fused into the attention
+
+QKN_PATS = ((32, 2),)
+
+
+def fqkn_fwd(lib, xq=Q, xk=K, v=V, gq=GQ, bq=BQ, gk=GK, bk=BK, eps=1e-5, out=OUT, lse=LSE, B=1,
+             N=64, H=4, Dh=64, pats=QKN_PATS, causal=1, dtype=_native.DA_BF16, scale=0.0):
+    arr = _native.pattern_array(pats)
+    return lib.dilated_attn_fwd_qknorm(xq, xk, v, gq, bq, gk, bk, eps, out, lse, B, N, H, Dh, arr,
+                                       len(pats), causal, dtype, scale, None)
+
+
+def fqkn_bwd(lib, xq=Q, xk=K, v=V, gq=GQ, bq=BQ, gk=GK, bk=BK, eps=1e-5, out=OUT, lse=LSE,
+             dout=DOUT, dxq=DQ, dxk=DK, dv=DV, dpar=DPAR, B=1, N=64, H=4, Dh=64, pats=QKN_PATS,
+             causal=1, dtype=_native.DA_BF16, scale=0.0, ws=WS, wsb=1 << 20):
+    arr = _native.pattern_array(pats)
+    return lib.dilated_attn_bwd_qknorm(xq, xk, v, gq, bq, gk, bk, eps, out, lse, dout, dxq, dxk,
+                                       dv, dpar, B, N, H, Dh, arr, len(pats), causal, dtype,
+                                       scale, ws, wsb, None)
+
+
+COMMON_FUSED_ERRORS = [
+    (dict(xq=None), -1), (dict(gq=None), -1), (dict(bk=None), -1),
+    (dict(N=60), -2), (dict(B=-1), -2),
+    (dict(pats=((16, 2), (32, 4))), -3),  # two patterns
+    (dict(pats=((64, 1),)), -3),          # 64 rows per segment
+    (dict(dtype=2), -4), (dict(Dh=128), -5),
+    (dict(gq=GQ + 8), -7), (dict(bk=BK + 4), -7),  # gains and biases: 16-byte aligned
+    (dict(eps=0.0), -9), (dict(eps=math.nan), -9), (dict(causal=3), -9),
+]
+
+
+@pytest.mark.parametrize("kwargs,code", COMMON_FUSED_ERRORS + [
+    (dict(out=GQ), -8), (dict(lse=BK), -8), (dict(out=None), -1),
+])
+def test_fused_qknorm_fwd_invalid_calls_rejected(lib, kwargs, code):
+    assert fqkn_fwd(lib, **kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs,code", COMMON_FUSED_ERRORS + [
+    (dict(dpar=None), -1), (dict(dout=None), -1),
+    (dict(ws=None), -6), (dict(wsb=1024), -6),
+    (dict(dpar=DPAR + 2), -7),
+    (dict(dpar=Q), -8), (dict(dpar=DQ + 64), -8), (dict(dpar=WS + 256), -8),
+    (dict(dxq=GK), -8), (dict(ws=GQ - 256), -8),
+])
+def test_fused_qknorm_bwd_invalid_calls_rejected(lib, kwargs, code):
+    assert fqkn_bwd(lib, **kwargs) == code
+
+
+def test_fused_qknorm_empty_problem_is_a_no_op(lib):
+    assert fqkn_fwd(lib, B=0, xq=None, xk=None, v=None, out=None, lse=None) == 0
+    assert fqkn_bwd(lib, N=0, xq=None, dxq=None, ws=None, wsb=0, dpar=None) == 0
+
+
+@pytest.mark.parametrize("B,N,H,w,r", [(32, 8192, 8, 64, 2), (1, 64, 4, 32, 2), (3, 240, 3, 40, 3),
+                                       (1, 32, 5, 64, 2)])
+def test_fused_qknorm_workspace_bytes(B, N, H, w, r):
+    """The plain backward's workspace, then float [2][units][128] partials,
+    then float [2][min(units, 1024)][128] folded sums, each region starting
+    on a 256-byte boundary; units = B * H * segments."""
+    up = lambda x: -(-x // 256) * 256
+    units = B * H * (N // min(w, N))
+    plain = _native.bwd_workspace_bytes(B, N, H, 64, [(w, r)], _native.DA_BF16)
+    exp = up(up(plain) + 2 * units * 128 * 4) + 2 * min(units, 1024) * 128 * 4
+    assert _native.bwd_qknorm_workspace_bytes(B, N, H, 64, [(w, r)], _native.DA_BF16) == exp
+
+
+def test_fused_qknorm_workspace_bytes_errors(lib):
+    out = ctypes.c_size_t(7)
+    arr = _native.pattern_array([(64, 1)])
+    assert lib.dilated_attn_bwd_qknorm_workspace_bytes(1, 64, 4, 64, arr, 1, 1,
+                                                       ctypes.byref(out)) == -3
+    arr = _native.pattern_array([(32, 2)])
+    assert lib.dilated_attn_bwd_qknorm_workspace_bytes(1, 64, 4, 64, arr, 1, 1, None) == -1
+    assert lib.dilated_attn_bwd_qknorm_workspace_bytes(0, 64, 4, 64, arr, 1, 1,
+                                                       ctypes.byref(out)) == 0
+    assert out.value == 0

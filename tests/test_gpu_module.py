@@ -93,6 +93,9 @@ CASES = [
     (1, 512, 4, 128, 4, False, True, False, "bf16"),
     (1, 512, 4, [128, 256, 512], [1, 2, 4], True, False, True, "bf16"),
     (1, 384, 3, [96, 384], [3, 6], False, False, True, "f32"),
+    # one pattern of at most 32 rows per segment: qk_norm inside the attention kernels
+    (2, 256, 2, 64, 2, True, False, True, "f32"),
+    (1, 240, 3, 40, 3, True, True, False, "bf16"),
 ]
 
 
