@@ -231,6 +231,7 @@ def run_module(args, dev):
     backward into x and every parameter) at the README's usage shape."""
     import torch
 
+    from sparse_long_sequence_attn_amd._native import bwd_qknorm_workspace_bytes
     from sparse_long_sequence_attn_amd.costs import PEAK_HBM_GBS, bwd_cost, cost
     from sparse_long_sequence_attn_amd.module import DilatedAttention
     from sparse_long_sequence_attn_amd.workloads import module_params, module_x
@@ -280,32 +281,56 @@ def run_module(args, dev):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / K
 
-    # the library's kernels on the step's own shapes, timed alone
-    from sparse_long_sequence_attn_amd import DA_BWD_KV, DA_BWD_MERGE, DA_BWD_PREP, DA_BWD_Q
-    from sparse_long_sequence_attn_amd import BwdProblem, Problem
+    # the library's kernels on the step's own shapes, timed alone: with
+    # qk_norm fused (one pattern of at most 32 rows per segment) the two
+    # fused calls, else the attention passes on normalised q and k
+    from sparse_long_sequence_attn_amd import (BwdProblem, Problem, dilated_attn_qknorm,
+                                               dilated_attn_qknorm_bwd, qk_norm_fwd)
 
-    from sparse_long_sequence_attn_amd import qk_norm_fwd
-
+    fused = mod._fused(x, B, N)
+    pats = list(mod.patterns)
     with torch.no_grad():
         shape = (B, N, heads, 64)
-        q, k = qk_norm_fwd(mod.to_q(x).view(shape), mod.to_k(x).view(shape), mod.q_norm.weight,
-                           mod.q_norm.bias, mod.k_norm.weight, mod.k_norm.bias, mod.q_norm.eps)
+        xq, xk = mod.to_q(x).view(shape), mod.to_k(x).view(shape)
         v = mod.to_v(x).view(shape).contiguous()
-    pats = list(mod.patterns)
-    fp = Problem(q, k, v, pats)
-    fp.run()
-    bp = BwdProblem(q, k, v, fp.out, fp.lse, torch.randn_like(q), pats)
+        gb = (mod.q_norm.weight, mod.q_norm.bias, mod.k_norm.weight, mod.k_norm.bias)
+        dout = torch.randn_like(v)
+        if fused:
+            out, lse = dilated_attn_qknorm(xq, xk, v, *gb, pats, mod.q_norm.eps)
+            ws = torch.empty(max(bwd_qknorm_workspace_bytes(B, N, heads, 64, pats, 1), 1),
+                             dtype=torch.uint8, device=dev)
+            grads = [torch.empty_like(v) for _ in range(3)]
+            dpar = torch.empty((2, 2, 64), dtype=torch.float32, device=dev)
+
+            def run_fwd():
+                dilated_attn_qknorm(xq, xk, v, *gb, pats, mod.q_norm.eps, out=out, lse=lse)
+
+            def run_bwd():
+                dilated_attn_qknorm_bwd(xq, xk, v, *gb, out, lse, dout, pats, mod.q_norm.eps,
+                                        workspace=ws, dxq=grads[0], dxk=grads[1], dv=grads[2],
+                                        dparams=dpar)
+        else:
+            q, k = qk_norm_fwd(xq, xk, *gb, mod.q_norm.eps) if c["qk_norm"] else (xq, xk)
+            fp = Problem(q, k, v, pats)
+            fp.run()
+            bp = BwdProblem(q, k, v, fp.out, fp.lse, dout, pats)
+
+            def run_fwd():
+                fp.attention_stage(stream)
+
+            def run_bwd():
+                bp.run(stream=stream)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     for _ in range(3):
-        fp.attention_stage(stream)
-        bp.run(DA_BWD_PREP | DA_BWD_KV | DA_BWD_Q | DA_BWD_MERGE, stream)
+        run_fwd()
+        run_bwd()
     reps = max(K, 10)
     ev[0].record(stream)
     for _ in range(reps):
-        fp.attention_stage(stream)
+        run_fwd()
     ev[1].record(stream)
     for _ in range(reps):
-        bp.run(DA_BWD_PREP | DA_BWD_KV | DA_BWD_Q | DA_BWD_MERGE, stream)
+        run_bwd()
     ev[2].record(stream)
     torch.cuda.synchronize()
     attn_ms = ev[0].elapsed_time(ev[1]) / reps
@@ -331,12 +356,15 @@ def run_module(args, dev):
                              "parallelism": "single GPU"}),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "attn_fwd_kernel (on the module's q, k, v)",
+                     "kernel": ("attn_fwd_kernel with qk_norm fused (on the module's xq, xk, v)"
+                                if fused else "attn_fwd_kernel (on the module's q, k, v)"),
                      "kernel_ms": round(attn_ms, 4)},
         "detail": {
             "attention_fwd_ms": round(attn_ms, 4),
             "attention_bwd_ms": round(bwd_ms, 4),
             "attention_share_of_step": round((attn_ms + bwd_ms) / ms_step, 4),
+            "qk_norm": ("fused into the attention kernels" if fused else
+                        "separate layer-norm kernels" if c["qk_norm"] else "off"),
             "attention_bwd_algorithmic_bytes": bc.kv_bytes + bc.q_bytes + bc.prep_bytes +
             bc.merge_bytes,
             "projection_gemm_flops": proj_flops,

@@ -737,18 +737,37 @@ __device__ inline void qkn_normalize(u32x4 (&r)[CK], const void* gain, const voi
   }
 }
 
+// The un-normalised input values write_rows_qkn needs, in its layout: row
+// 4 i + lane / 16, columns 4 (lane % 16) .. + 3 (rows past L read as zero).
+// Loaded ahead of the epilogue so the loads overlap the work before it.
+template <bool BF>
+using XRow = typename std::conditional<BF, u32x2, u32x4>::type;
+template <bool BF>
+__device__ inline void load_rows_x(XRow<BF> (&xw)[8], __amdgpu_buffer_rsrc_t rx, uint32_t mbytes,
+                                   int lane) {
+  const int sr = lane >> 4, sc = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t o = (uint32_t)(4 * i + sr) * mbytes;
+    if constexpr (BF)
+      xw[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, o + 8 * sc, 0, 0));
+    else
+      xw[i] = dev_load16(rx, o + 16 * sc);
+  }
+}
+
 // write_rows for a tensor that went through the fused qk_norm: the staged
 // rows are the gradient dy with respect to the normalised rows; with
-// g = dy * gain and xh = (x - mean) * rstd (x re-read from global memory)
-// each final row becomes dx = rstd * (g - mean(g) - xh * mean(g * xh)).
-// The lane's 4 columns of dy * xh and dy are summed over the rows it writes
-// and then over the wave into part[0 .. 2 kDh) (gain, then bias).
+// g = dy * gain and xh = (x - mean) * rstd (x from load_rows_x) each final
+// row becomes dx = rstd * (g - mean(g) - xh * mean(g * xh)). The lane's 4
+// columns of dy * xh and dy are summed over the rows it writes and then over
+// the wave into part[0 .. 2 kDh) (gain, then bias).
 template <bool BF>
 __device__ inline void write_rows_qkn(const float* srow, const int32_t* mpos,
                                       const int32_t* mkind, void* final_base, int64_t rs,
-                                      __amdgpu_buffer_rsrc_t rx, uint32_t mbytes,
-                                      const float* mean, const float* rstd, const void* gain,
-                                      float* part, int lane) {
+                                      const XRow<BF> (&xw)[8], const float* mean,
+                                      const float* rstd, const void* gain, float* part,
+                                      int lane) {
   using T = typename std::conditional<BF, __bf16, float>::type;
   const int sr = lane >> 4, sc = lane & 15;
   float gn[4], acc_g[4] = {0.f, 0.f, 0.f, 0.f}, acc_b[4] = {0.f, 0.f, 0.f, 0.f};
@@ -761,16 +780,14 @@ __device__ inline void write_rows_qkn(const float* srow, const int32_t* mpos,
     const f32x4 dy = *reinterpret_cast<const f32x4*>(srow + R * kStageStride + 4 * sc);
     float x[4];
     if constexpr (BF) {
-      const u32x2 w = __builtin_bit_cast(
-          u32x2, __builtin_amdgcn_raw_buffer_load_b64(rx, (uint32_t)R * mbytes + 8 * sc, 0, 0));
+      const u32x2 w = xw[i];
       x[0] = __uint_as_float(w[0] << 16);
       x[1] = __uint_as_float(w[0] & 0xffff0000u);
       x[2] = __uint_as_float(w[1] << 16);
       x[3] = __uint_as_float(w[1] & 0xffff0000u);
     } else {
-      const f32x4 w = __builtin_bit_cast(f32x4, dev_load16(rx, (uint32_t)R * mbytes + 16 * sc));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = w[e];
+      for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(xw[i][e]);
     }
     const float mu = mean[R], rs_ = rstd[R];
     float xh[4], gg[4], sg = 0.f, sgx = 0.f;
@@ -831,9 +848,11 @@ __device__ inline void write_rows_qkn(const float* srow, const int32_t* mpos,
 // through the LDS staging area as 128-byte lines.
 // QKN: the module's qk_norm fused in (a.qkn set; one pattern): q and k rows
 // are normalised while staged, and the dq, dk rows go through the layer
-// norm's backward before they are written.
+// norm's backward before they are written; bf16 with qk_norm is held to 168
+// VGPRs (3 waves per SIMD), which the early loads of the epilogue's input
+// rows would otherwise exceed.
 template <bool CAUSAL, bool BF, bool QKN = false>
-__global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(const BwdArgs a) {
   using T = typename std::conditional<BF, __bf16, float>::type;
   constexpr int ST = lds_stride<BF>();
   constexpr int kTileBytes = 32 * ST * (int)sizeof(T);
@@ -1018,6 +1037,8 @@ __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
                                                       dQ[db], 0, 0, 0);
       }
   }
+  XRow<BF> xq[QKN ? 8 : 1];  // QKN: q's input rows for the dq epilogue
+  if constexpr (QKN) load_rows_x<BF>(xq, rq, g.mbytes, lane);
   __syncthreads();  // tiles consumed: the staging area takes their place
 
   const PatDev& P = a.pat[tl.p];
@@ -1034,11 +1055,13 @@ __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
   }
   float* const part = a.ws + P.po_off + prow0 * kDh;
   stage_row(srow, dQ, a.scale, n, hh);
+  XRow<BF> xk[QKN ? 8 : 1];  // QKN: k's input rows for the dk epilogue
+  if constexpr (QKN) load_rows_x<BF>(xk, rk, g.mbytes, lane);
   __syncthreads();
   if constexpr (QKN) {
     const int64_t unit = prow0 / P.lmax;
-    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, rq,
-                       g.mbytes, qst, qst + 32, a.qkn[0], a.qkn_part + unit * 2 * kDh, lane);
+    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, xq,
+                       qst, qst + 32, a.qkn[0], a.qkn_part + unit * 2 * kDh, lane);
   } else {
     write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, part, lane);
   }
@@ -1047,9 +1070,9 @@ __global__ __launch_bounds__(64) void bwd_short_kernel(const BwdArgs a) {
   __syncthreads();
   if constexpr (QKN) {
     const int64_t unit = prow0 / P.lmax;
-    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs, rk,
-                       g.mbytes, qst + 64, qst + 96, a.qkn[2],
-                       a.qkn_part + (a.qkn_units + unit) * 2 * kDh, lane);
+    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs, xk,
+                       qst + 64, qst + 96, a.qkn[2], a.qkn_part + (a.qkn_units + unit) * 2 * kDh,
+                       lane);
   } else {
     write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs,
                    part + slots * kDh, lane);

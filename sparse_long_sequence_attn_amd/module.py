@@ -107,7 +107,9 @@ def _weight_grad(dy2, x2):
 
 class ProjectionFunction(torch.autograd.Function):
     """(y_1 .. y_n) = (x W_1^T + b_1, ..., x W_n^T + b_n) for one input x
-    [R, in]; the backward accumulates dx over the n products in place."""
+    [R, in]; the backward accumulates dx over the n products in place (an
+    out-of-place addmm would first copy its addend into a new [R, in]
+    tensor)."""
 
     @staticmethod
     def forward(ctx, x2, n, *wb):
@@ -123,7 +125,7 @@ class ProjectionFunction(torch.autograd.Function):
         dws, dbs = [], []
         for dy, w, hb in zip(dys, ws, ctx.has_bias):
             dy = dy.contiguous()
-            dx = torch.mm(dy, w) if dx is None else torch.addmm(dx, dy, w)
+            dx = torch.mm(dy, w) if dx is None else dx.addmm_(dy, w)
             dws.append(_weight_grad(dy, x2))
             dbs.append(dy.sum(0) if hb else None)
         return (dx, None, *dws, *dbs)
