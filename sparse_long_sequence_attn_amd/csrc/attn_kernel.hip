@@ -107,6 +107,17 @@ __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 with
+// the LDS bit): lane i's bytes land at dst + 16 i, whatever its offset;
+// offsets at or past the buffer's range write zeros. Device pass only: the
+// host pass has no such builtin and would drop the kernel's launch stub.
+typedef __attribute__((address_space(3))) char* lds_char_ptr;
+__device__ inline void dma_load16(__amdgpu_buffer_rsrc_t r, lds_char_ptr dst, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+#endif
+}
+
 // LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane m supplies 4 consecutive 16-bit elements; view them in lane order as
 // a 4 x 16 matrix (rows = lanes 4j..4j+3). Lane i receives column i:
@@ -129,10 +140,12 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool BF, int BN, int NBUF = 2>
+template <bool BF, int BN, int NBUF = 2, bool DMA = false>
 struct Smem {
-  // bf16: K [BN][64] swizzled, V [BN][72] (144-byte rows); fp32: K [BN][65], V [BN][64]
-  static constexpr int kVStride = BF ? kDh + 8 : kDh;
+  // bf16: K [BN][64] swizzled, V [BN][72] (144-byte rows), or with DMA (tiles
+  // written by the loads themselves) V [BN][64] swizzled; fp32: K [BN][65],
+  // V [BN][64]
+  static constexpr int kVStride = BF && !DMA ? kDh + 8 : kDh;
   static constexpr int kKElems = BF ? BN * kDh : BN * (kDh + 1);
   static constexpr int kVElems = BN * kVStride;
   static constexpr int kElemBytes = BF ? 2 : 4;
@@ -153,7 +166,10 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   // one-wave workgroups serve segments of at most 32 gathered rows (one key
   // tile): a single LDS buffer, so more workgroups fit on a CU
   constexpr int NBUF = NW == 1 ? 1 : 2;
-  using SM = Smem<BF, BN, NBUF>;
+  // bf16 multi-wave tiles go global -> LDS directly (buffer loads with the
+  // LDS bit): no staging registers and no LDS stores in the loop
+  constexpr bool DMA = BF && NBUF == 2;
+  using SM = Smem<BF, BN, NBUF, DMA>;
   constexpr int QW = 32 * QB;  // query rows per wave
   constexpr int BM = QW * NW;  // query rows per workgroup
   constexpr int NT = 64 * NW;
@@ -303,6 +319,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   const uint32_t tile_bytes = (uint32_t)BN * mbytes;
 
   auto load_tile = [&](int kt) {
+    if constexpr (DMA) return;
     const uint32_t base = (uint32_t)kt * tile_bytes;
 #pragma unroll
     for (int i = 0; i < CK; ++i) {
@@ -311,10 +328,42 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
     }
   };
 
+  // DMA: each load instruction fills 1 KiB of a tile, lane i the 16 bytes at
+  // i * 16 (measured); so lane i of the wave's instruction j fetches the
+  // chunk that belongs at that slot: row R = 8 (DW w + j) + i / 8, slot
+  // i % 8, which holds chunk (i % 8) ^ swizzle(R). K uses the swizzle of
+  // store_tile, V (row-major, 128-byte rows) XORs the chunk index with 4 on
+  // rows with bit 1 set, so the transpose reads of 4 consecutive rows hit
+  // 4 distinct quarters of the banks. Rows past L load zeros.
+  constexpr int DW = DMA ? BN * kRowBytes / 1024 / NW : 1;  // instructions per wave per tensor
+  static_assert(!DMA || (BN * kRowBytes) % (1024 * NW) == 0, "DMA tile split");
+  uint32_t dk_off[DW], dv_off[DW];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+      const int R = 8 * (DW * wv + j) + (lane >> 3), slot = lane & 7;
+      dk_off[j] = (uint32_t)R * mbytes + (uint32_t)((slot ^ ((R >> 1) & 7)) * 16);
+      dv_off[j] = (uint32_t)R * mbytes + (uint32_t)((slot ^ (((R >> 1) & 1) * 4)) * 16);
+    }
+  }
+  auto dma_tile = [&](int kt, int buf) {
+    if constexpr (DMA) {
+      const uint32_t base = (uint32_t)kt * tile_bytes;
+      const lds_char_ptr kl = (lds_char_ptr)smem + buf * SM::kKElems * 2;
+      const lds_char_ptr vl = (lds_char_ptr)smem + (NBUF * SM::kKElems + buf * SM::kVElems) * 2;
+#pragma unroll
+      for (int j = 0; j < DW; ++j) {
+        dma_load16(rk, kl + (DW * wv + j) * 1024, base + dk_off[j]);
+        dma_load16(rv, vl + (DW * wv + j) * 1024, base + dv_off[j]);
+      }
+    }
+  };
+
   // K rows: 16-byte chunk j of row x goes to slot j ^ ((x >> 1) & 7), so the
   // 16 lanes the LDS serves together (rows x..x+15, one chunk index each)
   // hit 16 distinct 16-byte bank groups of the 256-byte bank window.
   auto store_tile = [&](int buf) {
+    if constexpr (DMA) return;
     T* K = Ks + buf * SM::kKElems;
     T* V = Vs + buf * SM::kVElems;
     if constexpr (QKN) {
@@ -533,6 +582,47 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
           (NBUF * SM::kKElems + buf * SM::kVElems) * sizeof(T);
       const uint32_t vlane = (uint32_t)((4 * (g16 >> 1) + (m16 >> 2)) * SM::kVStride +
                                         16 * (g16 & 1) + 4 * (m16 & 3)) * 2;
+      if constexpr (DMA) {
+        static_assert(KB == 2 && SM::kVStride == kDh, "DMA PV reads: 64-key tiles, 128-byte rows");
+        // the 64-byte half db of row 16c + 8h + rr sits at half
+        // db ^ ((rr >> 1) & 1) of that row. The reads are written out (all
+        // eight fragment pairs of a half, then one wait, in one statement):
+        // the compiler's own transpose reads would each wait for the next
+        // tile's loads, which write the other buffer. The outputs are
+        // early-clobber: no fragment may share a register with the address.
+        const uint32_t vswz = (uint32_t)((m16 >> 3) & 1);
+        const uint32_t vrow = (uint32_t)reinterpret_cast<uintptr_t>(vbase) + vlane;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const uint32_t addr = vrow + 64u * ((uint32_t)db ^ vswz);
+          u32x2 f[8];  // (lo, hi) for c = 0..3
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %8\n\t"
+              "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+              "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
+              "ds_read_b64_tr_b16 %3, %8 offset:3072\n\t"
+              "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
+              "ds_read_b64_tr_b16 %5, %8 offset:5120\n\t"
+              "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
+              "ds_read_b64_tr_b16 %7, %8 offset:7168\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+                "=&v"(f[6]), "=&v"(f[7])
+              : "v"(addr)
+              : "memory");
+#pragma unroll
+          for (int c = 0; c < 2 * KB; ++c) {
+            if (c >= 2 * nkb) break;
+            const bf16x8 vf =
+                __builtin_bit_cast(bf16x8, u32x4{f[2 * c][0], f[2 * c][1], f[2 * c + 1][0],
+                                                 f[2 * c + 1][1]});
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  vf, __builtin_bit_cast(bf16x8, pw[qb][c]), O[db][qb], 0, 0, 0);
+          }
+        }
+      } else {
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -547,6 +637,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
             O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 vf, __builtin_bit_cast(bf16x8, pw[qb][c]), O[db][qb], 0, 0, 0);
         }
+      }
       }
     } else {
       float pf[QB][KB][16];
@@ -580,12 +671,22 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   // ---- main loop over key tiles, double-buffered through LDS
   load_tile(0);
   store_tile(0);
+  dma_tile(0, 0);
   // every load issued so far (the query fragments included) completes here:
   // otherwise the loop's first use of the fragments waits on the global
   // loads the loop itself has just issued for the next tile
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (NBUF == 2) {
+  if constexpr (DMA) {
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      // the other buffer was last read before the previous barrier
+      if (kt + 1 < nkt) dma_tile(kt + 1, buf ^ 1);
+      if (kt < nkt_w) compute(buf, kt);
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's tile writes have landed
+      __syncthreads();
+    }
+  } else if constexpr (NBUF == 2) {
     for (int kt = 0; kt < nkt; ++kt) {
       const int buf = kt & 1;
       if (kt + 1 < nkt) load_tile(kt + 1);
