@@ -522,7 +522,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   constexpr int KBT = BK / 32;
   constexpr int NT = 64 * NW;
   constexpr int ST = lds_stride<BF>();
-  constexpr int kTileBytes = BK * ST * (int)sizeof(T);
+  // bf16: K and V tiles loaded straight into LDS (128-byte rows, chunks at
+  // dma_slot); fp32: staged through registers into padded rows
+  constexpr int kTileBytes = BF ? BK * kDh * 2 : BK * ST * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes;  // K, V
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
   __shared__ __attribute__((aligned(16))) char smem[2 * kBufBytes];
@@ -569,16 +571,35 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   const int32_t qend_w = min(g.L, qw0 + 32);
   const int32_t nkt_w = qw0 >= g.L ? 0 : (CAUSAL ? (qend_w + BK - 1) / BK : nkt);
 
-  PairStager<BF, BK, NT> stg;
-  stg.init(tid, g.mbytes);
-  auto load_tile = [&](int t) { stg.load(rk, rv, (uint32_t)(t * BK) * g.mbytes); };
+  PairStager<BF, BF ? NT / 8 : BK, NT> stg;  // fp32 only
+  DmaTile<BK, NW> dmt;                      // bf16 only
+  if constexpr (BF)
+    dmt.init(wv, lane, g.mbytes);
+  else
+    stg.init(tid, g.mbytes);
+  // bf16: tile t into buffer buf; fp32: tile t into registers
+  auto load_tile = [&](int t, int buf) {
+    if constexpr (BF) {
+      const lds_ptr kt = (lds_ptr)smem + buf * kBufBytes;
+      dmt.load(rk, kt, (uint32_t)(t * BK) * g.mbytes, wv);
+      dmt.load(rv, kt + kTileBytes, (uint32_t)(t * BK) * g.mbytes, wv);
+    } else {
+      stg.load(rk, rv, (uint32_t)(t * BK) * g.mbytes);
+    }
+  };
   auto store_tile = [&](int buf) {
-    char* base = smem + buf * kBufBytes;
-    stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
+    if constexpr (!BF) {
+      char* base = smem + buf * kBufBytes;
+      stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
+    }
   };
 
   const float sl2 = a.sl2;
-  const uint32_t trl = tr_lane_offset<ST>(lane);
+  uint32_t trk[2][2];  // bf16: transpose-read offsets (dma_tr_offset)
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) trk[db][h] = BF ? dma_tr_offset(lane, h, db) : 0u;
 
   auto compute = [&](int buf, int t) {
     const char* base = smem + buf * kBufBytes;
@@ -596,8 +617,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
       if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + row * ST + 16 * ks + 8 * hh);
-          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + row * ST + 16 * ks + 8 * hh);
+          const int o = row * kDh + dma_slot(row, 2 * ks + hh) * 8;
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + o);
+          const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vs + o);
           S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf.x[ks], S, 0, 0, 0);
           dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df.x[ks], dP, 0, 0, 0);
         }
@@ -625,16 +647,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
       else
         probs(false);
       if constexpr (BF) {
-        const lds_cptr kbase = (lds_cptr)smem + buf * kBufBytes;
+        const uint32_t kaddr = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)smem) +
+                               (uint32_t)(buf * kBufBytes + kb * 32 * 128);
+        uint32_t ad[2][2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) ad[db][h] = kaddr + trk[db][h];
+        bf16x8 kfr[2][2];
+        dma_tr_read8(kfr, ad);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x8 sb = to_bf16x8(sv + 8 * c);
 #pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const uint32_t o = trl + (uint32_t)((kb * 32 + 16 * c) * ST + db * 32) * 2;
-            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(kbase, o, ST), sb, dQ[db],
-                                                             0, 0, 0);
-          }
+          for (int db = 0; db < 2; ++db)
+            dQ[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[db][c], sb, dQ[db], 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -649,14 +676,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
     }
   };
 
-  load_tile(0);
+  load_tile(0, 0);
   store_tile(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < nkt; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nkt) load_tile(t + 1);
+    // the other buffer was last read before the previous barrier
+    if (t + 1 < nkt) load_tile(t + 1, buf ^ 1);
     if (t < nkt_w) compute(buf, t);
     if (t + 1 < nkt) store_tile(buf ^ 1);
+    if constexpr (BF) __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
     __syncthreads();
   }
 
