@@ -482,6 +482,28 @@ def main():
     matmul_tflops = 2.0 * 8192 ** 3 / (mev[0].elapsed_time(mev[1]) / 10 / 1e3) / 1e12
     del a_m, b_m
 
+    # the one-pass variant (one launch, every covering pattern in one online
+    # softmax, no merge pass) on the same inputs, for comparison
+    onepass_ms = None
+    if w.dtype == "bf16" and len(w.patterns) > 1:
+        from sparse_long_sequence_attn_amd import DilatedAttnError, dilated_attn_onepass
+
+        o1, l1 = torch.empty_like(q), torch.empty_like(prob.lse)
+        try:
+            for _ in range(3):
+                dilated_attn_onepass(q, k, v, w.patterns, w.causal, out=o1, lse=l1)
+            oev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(10)]
+            for e0, e1 in oev:
+                e0.record(stream)
+                dilated_attn_onepass(q, k, v, w.patterns, w.causal, out=o1, lse=l1)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            onepass_ms = sorted(a.elapsed_time(b) for a, b in oev)[5]
+        except DilatedAttnError:  # the pattern list has no one-pass form
+            onepass_ms = None
+        del o1, l1
+
     c = cost(w.B, w.N, w.H, w.Dh, w.patterns, w.causal, 2 if w.dtype == "bf16" else 4)
     tokens_s = w.tokens / (ms_step / 1e3)
     peak = peak_tflops(w.dtype)
@@ -539,6 +561,9 @@ def main():
             "merge_algorithmic_bytes": c.merge_bytes,
             "merge_gbs_algorithmic": round(c.merge_bytes / (merge_ms / 1e3) / 1e9, 1)
             if merge_ms > 0 and c.merge_bytes > 0 else None,
+            "onepass_step_ms_median": round(onepass_ms, 4) if onepass_ms else None,
+            "onepass_tflops_algorithmic": round(c.flops_alg / (onepass_ms / 1e3) / 1e12, 2)
+            if onepass_ms else None,
             "device": torch.cuda.get_device_name(dev),
         },
     }

@@ -263,6 +263,25 @@ int dilated_attn_bwd_qknorm(const void* xq, const void* xk, const void* v, const
                             int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------ one pass
+ *
+ * The forward of dilated_attn_fwd in a single launch, with no workspace and
+ * no merge pass (bf16 only; DA_ERR_DTYPE for fp32). Each row's merged
+ * output is one softmax over every (pattern, key) pair its covering
+ * patterns give it (the LSE merge of the per-pattern results, reading of
+ * the LONGNET blog's "Dilated Attention" mixture and the dakule.com news
+ * article's pattern list), so a workgroup streams the keys of every pattern
+ * that covers its rows through one online softmax and writes final rows.
+ * Rows are grouped by position residue mod L = lcm(r) inside windows of
+ * W = gcd(min(w, N)) positions, which every pattern covers all or none of.
+ * DA_ERR_PATTERN when L > W. Arguments, checks and outputs as
+ * dilated_attn_fwd without the workspace; results equal dilated_attn_fwd's
+ * up to rounding order. */
+int dilated_attn_fwd_onepass(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t N, int32_t H, int32_t Dh,
+                             const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                             int32_t dtype, float scale, void* stream);
+
 /* Test hook: the gather map the kernels use, written by a device kernel
  * through the same index function as the attention kernel.
  * dev_out: device int64 [N / min(w, N)][ceil(min(w, N) / r)], segment-major;

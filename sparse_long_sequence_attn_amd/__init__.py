@@ -19,7 +19,7 @@ __all__ = [
     "DA_F32", "DA_BF16", "DA_HEAD_DIM", "DA_MAX_PATTERNS", "Problem", "dilated_attn_bwd",
     "BwdProblem", "bwd_workspace_bytes", "DA_BWD_PREP", "DA_BWD_KV", "DA_BWD_Q", "DA_BWD_MERGE",
     "DA_BWD_ALL", "qk_norm_fwd", "qk_norm_bwd", "qknorm_fused_supported", "dilated_attn_qknorm",
-    "dilated_attn_qknorm_bwd",
+    "dilated_attn_qknorm_bwd", "dilated_attn_onepass",
 ]
 
 
@@ -163,6 +163,31 @@ def dilated_attn_bwd(q, k, v, out, lse, dout, patterns, causal=True, scale=None,
 def dilated_attn(q, k, v, patterns, causal=True, scale=None, out=None, lse=None, workspace=None):
     """Dilated-attention forward. Returns (out, lse); see include/dilated_attn.h."""
     return Problem(q, k, v, patterns, causal, scale, out, lse, workspace).run()
+
+
+def dilated_attn_onepass(q, k, v, patterns, causal=True, scale=None, out=None, lse=None):
+    """The forward in one launch (bf16): every row's covering patterns run
+    through one online softmax, no workspace and no merge pass. Returns
+    (out, lse); see include/dilated_attn.h."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor; no CPU path exists")
+        if t.dim() != 4 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous [B, N, H, Dh] tensor like q")
+    B, N, H, Dh = (int(x) for x in q.shape)
+    pats = [(int(w), int(r)) for (w, r) in patterns]
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_out("out", out, q.shape, q.dtype, q.device)
+    _check_out("lse", lse, (B, H, N), torch.float32, q.device)
+    code = load_library().dilated_attn_fwd_onepass(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, N, H, Dh,
+        _native.pattern_array(pats), len(pats), 1 if causal else 0, _dtype_code(q),
+        float(scale) if scale else 0.0, torch.cuda.current_stream(q.device).cuda_stream)
+    _native.check(code, "dilated_attn_fwd_onepass")
+    return out, lse
 
 
 def dilated_attn_attention_stage(prob, stream=None):

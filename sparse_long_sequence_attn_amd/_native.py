@@ -49,6 +49,7 @@ SIGNATURES = {
     "dilated_attn_qk_norm_workspace_bytes": ([_I64, ctypes.POINTER(_SZ)], ctypes.c_int),
     "dilated_attn_qk_norm_bwd": ([_P] * 9 + [_I64, _I32, _I32, ctypes.c_float, _P, _SZ, _P],
                                  ctypes.c_int),
+    "dilated_attn_fwd_onepass": (_FWD_ARGS[:-3] + [_P], ctypes.c_int),
     "dilated_attn_fwd_qknorm": ([_P] * 7 + [ctypes.c_float, _P, _P, _I64, _I64, _I32, _I32, _P,
                                            _I32, _I32, _I32, ctypes.c_float, _P], ctypes.c_int),
     "dilated_attn_bwd_qknorm_workspace_bytes": ([_I64, _I64, _I32, _I32, _P, _I32, _I32,

@@ -480,6 +480,63 @@ int dilated_attn_fwd(const void* q, const void* k, const void* v, void* out, flo
                     scale, workspace, workspace_bytes, stream);
 }
 
+// One-pass geometry: L = lcm of the dilation rates, W = gcd of the
+// effective segment lengths; DA_ERR_PATTERN where the one-pass form does not
+// apply (L above W: fewer than one row per residue and window).
+int onepass_geometry(const Plan& pl, da::OnePassArgs* a, int64_t* grid) {
+  int64_t L = 1, W = 0;
+  for (int i = 0; i < pl.np; ++i) {
+    const int64_t r = pl.pat[i].r;
+    L = L / std::__gcd(L, r) * r;
+    if (L > (int64_t)1 << 20) return DA_ERR_PATTERN;
+    W = std::__gcd(W, pl.pat[i].wp);
+  }
+  if (L > W) return DA_ERR_PATTERN;
+  const int64_t per_res = (W + L - 1) / L;  // rows of the fullest residue in a window
+  a->L = (int32_t)L;
+  a->W = (int32_t)W;
+  constexpr int64_t bm = 32 * da::kOnePassWaves;
+  a->nblk = (int32_t)((per_res + bm - 1) / bm);
+  a->nwin = pl.N / W;
+  const int64_t groups = pl.B * pl.H * a->nwin;
+  *grid = (groups + da::kXcds - 1) / da::kXcds * da::kXcds * L * a->nblk;
+  return *grid > kMaxGrid ? DA_ERR_SHAPE : DA_OK;
+}
+
+int dilated_attn_fwd_onepass(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t N, int32_t H, int32_t Dh,
+                             const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                             int32_t dtype, float scale, void* stream) {
+  Plan pl;
+  int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
+  if (rc != DA_OK) return rc;
+  if (!pl.bf16) return DA_ERR_DTYPE;
+  if (pl.empty) return DA_OK;
+  da::OnePassArgs a;
+  memset(&a, 0, sizeof a);
+  int64_t grid = 0;
+  rc = onepass_geometry(pl, &a, &grid);
+  if (rc != DA_OK) return rc;
+  Plan chk = pl;  // no workspace
+  chk.ws_bytes = 0;
+  rc = check_buffers(chk, q, k, v, out, lse, nullptr, 0);
+  if (rc != DA_OK) return rc;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.B = pl.B;
+  a.N = pl.N;
+  a.H = pl.H;
+  a.np = pl.np;
+  a.sl2 = pl.sl2;
+  for (int i = 0; i < pl.np; ++i) a.pat[i] = pl.pat[i];
+  const hipError_t e =
+      da::launch_onepass(a, pl.causal, grid, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
 int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
                             const void* bias_q, const void* gain_k, const void* bias_k,
                             float eps, void* out, float* lse, int64_t B, int64_t N, int32_t H,

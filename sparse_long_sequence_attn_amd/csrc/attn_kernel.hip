@@ -882,6 +882,304 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   }
 }
 
+// ---------------------------------------------------------------- one pass
+
+// Geometry of one covering pattern for a one-pass workgroup (all
+// wave-uniform): its gathered key rows in the segment that holds the
+// group, and the group's rows as gathered indices j0 + s m of that pattern.
+struct OnePat {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t mbytes;  // bytes between consecutive gathered rows
+  int32_t Lp;       // rows the head gathers from the segment
+  int32_t j0;       // gathered index of group row 0
+  int32_t s;        // L / r: gathered rows between consecutive group rows
+  int32_t nkt;      // key tiles the workgroup needs
+};
+
+// bf16, kOnePassWaves waves x 32 group rows, 64-key tiles loaded straight into LDS (the
+// layouts of attn_fwd_kernel's 4-wave path); the key tiles of all covering
+// patterns go through one online softmax, and every row is written final.
+template <bool CAUSAL>
+__global__ __launch_bounds__(64 * kOnePassWaves, 4) void attn_onepass_kernel(const OnePassArgs a) {
+  constexpr int NW = kOnePassWaves, BN = 64, KB = BN / 32, BM = 32 * NW;
+  constexpr int DW = BN * 128 / 1024 / NW;
+  using T = __bf16;
+  using SM = Smem<true, BN, 2, true>;
+  __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
+
+  // ---- block -> (batch, head, window, residue, row block). The L * nblk
+  // workgroups of one (batch, head, window), which read the same key rows,
+  // run on one XCD; those groups are dealt to the XCDs round-robin.
+  const int64_t id = blockIdx.x;
+  const int32_t xcd = (int32_t)(id % kXcds);
+  const int64_t slot = id / kXcds;
+  const int64_t per = (int64_t)a.L * a.nblk;
+  const int64_t grp = xcd + kXcds * (slot / per);
+  if (grp >= a.B * a.H * a.nwin) return;
+  const int32_t mem = (int32_t)(slot % per);
+  const int32_t res = mem / a.nblk;
+  const int32_t blk = a.nblk - 1 - mem % a.nblk;  // later rows (more keys) first
+  const int64_t win = grp % a.nwin;
+  const int64_t bh = grp / a.nwin;
+  const int32_t h = (int32_t)(bh % a.H);
+  const int64_t b = bh / a.H;
+
+  const int64_t w0 = win * a.W;
+  const int32_t rho = (int32_t)((res - w0 % a.L + a.L) % a.L);  // t0 - w0
+  const int32_t cnt = rho < a.W ? (a.W - rho + a.L - 1) / a.L : 0;
+  const int32_t q0 = blk * BM;
+  if (q0 >= cnt) return;
+  const int64_t t0 = w0 + rho;  // position of group row 0
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int64_t rs = (int64_t)a.H * kDh;
+  const int64_t headbase = b * a.N * rs + (int64_t)h * kDh;
+  const int32_t qw0 = q0 + 32 * wv;  // this wave's first group row
+  const int32_t mq = qw0 + n;        // this lane's row
+  const int32_t qend_wg = min(cnt, q0 + BM);
+  const int32_t qend_w = min(cnt, qw0 + 32);
+  T* const orow = reinterpret_cast<T*>(a.out) + headbase;
+  float* const lse_row = a.lse + bh * a.N;
+
+  // ---- covering patterns: those whose head offset matches the group's
+  // position inside its segment (the same for every row of the group)
+  uint32_t cover = 0;
+  for (int p = 0; p < a.np; ++p) {
+    const PatDev& P = a.pat[p];
+    const int32_t off = head_offset(h, P.r);
+    const int64_t u = t0 % P.wp;  // position inside the segment
+    if (off < P.wp && u >= off && (u - off) % P.r == 0) cover |= 1u << p;
+  }
+  if (cover == 0) {
+    // no pattern gathers these positions: 0 and -inf
+    const int sr = lane >> 4, sc = lane & 15;
+    for (int m = qw0 + sr; m < qend_w; m += 4) {
+      const int64_t t = t0 + (int64_t)a.L * m;
+      *reinterpret_cast<u32x2*>(orow + t * rs + 4 * sc) = u32x2{0u, 0u};
+      if (sc == 0) lse_row[t] = -INFINITY;
+    }
+    return;
+  }
+  auto make_pat = [&](int p) {
+    const PatDev& P = a.pat[p];
+    OnePat o;
+    const int32_t off = head_offset(h, P.r);
+    const int64_t seg0 = t0 - t0 % P.wp;
+    o.Lp = rows_gathered(P.wp, off, P.r);
+    o.j0 = (int32_t)((t0 - seg0 - off) / P.r);
+    o.s = a.L / P.r;
+    o.mbytes = (uint32_t)((int64_t)P.r * rs * 2);
+    const uint32_t range = (uint32_t)(o.Lp - 1) * o.mbytes + kDh * 2;
+    const int64_t base = headbase + (seg0 + off) * rs;
+    o.rk = make_rsrc(reinterpret_cast<const T*>(a.k) + base, range);
+    o.rv = make_rsrc(reinterpret_cast<const T*>(a.v) + base, range);
+    const int32_t kend = CAUSAL ? o.j0 + o.s * (qend_wg - 1) + 1 : o.Lp;
+    o.nkt = (kend + BN - 1) / BN;
+    return o;
+  };
+  auto next_pat = [&](int p) {  // next covering pattern after p, or a.np
+    const uint32_t rest = p + 1 < 32 ? cover >> (p + 1) : 0u;
+    return rest ? p + 1 + __builtin_ctz(rest) : a.np;
+  };
+
+  // ---- query fragments: group rows at stride L positions
+  const uint32_t qbytes = (uint32_t)((int64_t)a.L * rs * 2);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(reinterpret_cast<const T*>(a.q) + headbase + t0 * rs,
+                (uint32_t)(cnt - 1) * qbytes + kDh * 2);
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = __builtin_bit_cast(bf16x8,
+                                buf_load16(rq, (uint32_t)mq * qbytes + (16 * ks + 8 * hh) * 2));
+
+  // ---- key/value tiles straight into LDS (the swizzles of attn_fwd_kernel)
+  auto dma_tile = [&](const OnePat& o, int kt, int buf) {
+    const uint32_t base = (uint32_t)(kt * BN) * o.mbytes;
+    const lds_char_ptr kl = (lds_char_ptr)smem + buf * SM::kKElems * 2;
+    const lds_char_ptr vl = (lds_char_ptr)smem + (2 * SM::kKElems + buf * SM::kVElems) * 2;
+#pragma unroll
+    for (int j = 0; j < DW; ++j) {
+      const int R = 8 * (DW * wv + j) + (lane >> 3), sl = lane & 7;
+      const uint32_t ro = base + (uint32_t)R * o.mbytes;
+      dma_load16(o.rk, kl + (DW * wv + j) * 1024, ro + (uint32_t)((sl ^ ((R >> 1) & 7)) * 16));
+      dma_load16(o.rv, vl + (DW * wv + j) * 1024, ro + (uint32_t)((sl ^ (((R >> 1) & 1) * 4)) * 16));
+    }
+  };
+
+  f32x16 O[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) O[db][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  bool started = false;  // a tile has set the running max (wave-uniform)
+  const float sl2 = a.sl2;
+  const int m16 = lane & 15, g16 = lane >> 4;
+  const uint32_t vlane = (uint32_t)((4 * (g16 >> 1) + (m16 >> 2)) * kDh + 16 * (g16 & 1) +
+                                    4 * (m16 & 3)) * 2;
+  const uint32_t vswz = (uint32_t)((m16 >> 3) & 1);
+
+  auto compute = [&](const OnePat& o, int buf, int kt) {
+    const T* K = reinterpret_cast<const T*>(smem) + buf * SM::kKElems;
+    // the keys some row of the wave sees: up to its last row's gathered
+    // index (causal) or the segment's rows
+    const int32_t kend = CAUSAL ? o.j0 + o.s * (qend_w - 1) + 1 : o.Lp;
+    const int nkb = __builtin_amdgcn_readfirstlane(min(KB, (kend - kt * BN + 31) / 32));
+    f32x16 S[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb >= nkb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[kb][v] = -INFINITY;
+        continue;
+      }
+      S[kb] = f32x16{};
+      const int row = kb * 32 + n;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            K + row * kDh + (((2 * ks + hh) ^ ((row >> 1) & 7)) << 3));
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kb], 0, 0, 0);
+      }
+    }
+    // mask: causal - key j is seen by row m when j <= j0 + s m (its own
+    // position or earlier); non-causal - keys past the segment's rows
+    const int32_t thr = o.j0 + o.s * mq;
+    const int32_t thr_w = __builtin_amdgcn_readfirstlane(o.j0 + o.s * qw0);  // the wave's lowest
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb >= nkb) continue;
+      const int32_t kb0 = kt * BN + kb * 32;
+      if (CAUSAL ? kb0 + 31 > thr_w : kb0 + 32 > o.Lp) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int32_t key = kb0 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (CAUSAL ? key > thr : key >= o.Lp) S[kb][v] = -INFINITY;
+        }
+      }
+    }
+
+    // lazy rescale and P exactly as in attn_fwd_kernel
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][v]);
+    const float mt = pair_max(mx) * sl2;
+    if (!started) {
+      m_run = mt;
+      started = true;
+    } else if (__ballot(mt > m_run + 8.f) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = exp2_fast(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) O[db] *= alpha;
+    }
+    u32x4 pw[2 * KB];
+    float lsum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2 * KB; ++c) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e], sl2, -m_run));
+        const float p1 = exp2_fast(fmaf(S[c >> 1][8 * (c & 1) + e + 1], sl2, -m_run));
+        bf16x2 pr;
+        pr[0] = (__bf16)p0;
+        pr[1] = (__bf16)p1;
+        pw[c][e >> 1] = __builtin_bit_cast(uint32_t, pr);
+        const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
+      }
+    }
+    l_run += lsum;
+    // O^T += V^T P^T, V^T from the transpose reads (one statement per half,
+    // as in attn_fwd_kernel)
+    const uint32_t vrow = (uint32_t)reinterpret_cast<uintptr_t>(
+                              (lds_char_ptr)smem + (2 * SM::kKElems + buf * SM::kVElems) * 2) +
+                          vlane;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const uint32_t addr = vrow + 64u * ((uint32_t)db ^ vswz);
+      u32x2 f[8];
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %8\n\t"
+          "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+          "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %3, %8 offset:3072\n\t"
+          "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
+          "ds_read_b64_tr_b16 %5, %8 offset:5120\n\t"
+          "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
+          "ds_read_b64_tr_b16 %7, %8 offset:7168\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]),
+            "=&v"(f[6]), "=&v"(f[7])
+          : "v"(addr)
+          : "memory");
+#pragma unroll
+      for (int c = 0; c < 2 * KB; ++c) {
+        if (c >= 2 * nkb) break;
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, u32x4{f[2 * c][0], f[2 * c][1], f[2 * c + 1][0], f[2 * c + 1][1]});
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pw[c]),
+                                                        O[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- the key tiles of every covering pattern, double-buffered
+  int p = next_pat(-1);
+  OnePat cur = make_pat(p);
+  int kt = 0, buf = 0;
+  dma_tile(cur, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (;;) {
+    int np_ = p, nkt_ = kt + 1;
+    OnePat nxt = cur;
+    if (nkt_ >= cur.nkt) {
+      np_ = next_pat(p);
+      nkt_ = 0;
+      if (np_ < a.np) nxt = make_pat(np_);
+    }
+    const bool more = np_ < a.np;
+    if (more) dma_tile(nxt, nkt_, buf ^ 1);  // the other buffer was last read before the barrier
+    if (qw0 < cnt) {
+      const int32_t kend_w = CAUSAL ? cur.j0 + cur.s * (qend_w - 1) + 1 : cur.Lp;
+      if (kt * BN < kend_w) compute(cur, buf, kt);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
+    __syncthreads();
+    if (!more) break;
+    p = np_;
+    kt = nkt_;
+    cur = nxt;
+    buf ^= 1;
+  }
+
+  // ---- every row is final: out and lse written directly
+  if (mq >= cnt) return;
+  const float l_tot = pair_sum(l_run);
+  const float inv = __builtin_amdgcn_rcpf(l_tot);
+  const int64_t t = t0 + (int64_t)a.L * mq;
+  T* const dst = orow + t * rs + 4 * hh;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      *reinterpret_cast<u32x2*>(dst + db * 32 + 8 * g) =
+          u32x2{pack_bf16_rne(O[db][4 * g] * inv, O[db][4 * g + 1] * inv),
+                pack_bf16_rne(O[db][4 * g + 2] * inv, O[db][4 * g + 3] * inv)};
+    }
+  if (hh == 0) lse_row[t] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
 template <int NW, int QB, int BN, bool BF>
 hipError_t launch_cfg(const AttnArgs& a, bool causal, bool final_out, int64_t grid,
                       hipStream_t st) {
@@ -923,6 +1221,15 @@ hipError_t launch_attention_qkn(const AttnArgs& a, bool bf16, bool causal, int64
     else
       hipLaunchKernelGGL((attn_fwd_kernel<1, 1, 32, false, true, false, true>), g, b, 0, st, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_onepass(const OnePassArgs& a, bool causal, int64_t grid, hipStream_t st) {
+  const dim3 g((uint32_t)grid), b(64 * kOnePassWaves);
+  if (causal)
+    hipLaunchKernelGGL(attn_onepass_kernel<true>, g, b, 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_onepass_kernel<false>, g, b, 0, st, a);
   return hipGetLastError();
 }
 

@@ -85,6 +85,36 @@ struct AttnArgs {
   int64_t unit_start[kMaxPat + 1];  // first global unit of each sorted pattern
 };
 
+// Single-launch forward: the patterns' merge folded into one online
+// softmax. With reading R1 a row's merged output is one softmax over every
+// (pattern, key) pair its covering patterns give it, so a workgroup can run
+// its queries through the keys of every covering pattern in turn and write
+// final rows. Positions are grouped by residue mod L = lcm(r) inside windows
+// of W = gcd(w') positions: every pattern covers all or none of a group (its
+// r divides L, and its segments start at multiples of W), and a window lies
+// inside one segment of every pattern. A workgroup takes up to
+// 32 kOnePassWaves positions (rows m of the group at t0 + L m) of one
+// (batch, head, window, residue) group.
+constexpr int kOnePassWaves = 4;  // waves (32 group rows each) per one-pass workgroup
+
+struct OnePassArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int64_t B;
+  int64_t N;
+  int32_t H;
+  int32_t np;
+  float sl2;     // softmax scale * log2(e)
+  int32_t L;     // lcm of the dilation rates
+  int32_t W;     // gcd of the effective segment lengths
+  int32_t nblk;  // workgroups per (window, residue): ceil(ceil(W / L) / (32 kOnePassWaves))
+  int64_t nwin;  // N / W
+  PatDev pat[kMaxPat];  // caller's order
+};
+
 struct MergeArgs {
   void* out;
   float* lse;

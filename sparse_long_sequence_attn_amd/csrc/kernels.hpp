@@ -18,6 +18,8 @@ hipError_t launch_attention(const AttnArgs& a, bool bf16, int nw, bool causal, b
 // The one-wave attention kernel with the module's qk_norm applied to q and k
 // as they are loaded (a.qkn, a.qkn_eps set; one pattern, segments of at most
 // 32 gathered rows, final outputs).
+// One-pass forward (bf16): grid = kXcds * ceil(B H nwin / kXcds) * L * nblk.
+hipError_t launch_onepass(const OnePassArgs& a, bool causal, int64_t grid, hipStream_t st);
 hipError_t launch_attention_qkn(const AttnArgs& a, bool bf16, bool causal, int64_t grid,
                                 hipStream_t st);
 

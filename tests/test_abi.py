@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_native.SIGNATURES)
@@ -365,3 +365,31 @@ def test_fused_qknorm_workspace_bytes_errors(lib):
     assert lib.dilated_attn_bwd_qknorm_workspace_bytes(0, 64, 4, 64, arr, 1, 1,
                                                        ctypes.byref(out)) == 0
     assert out.value == 0
+
+
+# ---------------------------------------------------------------- one-pass forward
+
+
+def onepass(lib, q=Q, k=K, v=V, out=OUT, lse=LSE, B=1, N=64, H=4, Dh=64, pats=((16, 2), (32, 4)),
+            causal=1, dtype=_native.DA_BF16, scale=0.0):
+    arr = _native.pattern_array(pats)
+    return lib.dilated_attn_fwd_onepass(q, k, v, out, lse, B, N, H, Dh, arr, len(pats), causal,
+                                        dtype, scale, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(N=60), -2), (dict(B=-1), -2),
+    (dict(pats=((16, 0),)), -3), (dict(pats=((16, 2),) * 9), -3),
+    (dict(pats=((8, 5), (8, 7))), -3),  # lcm(r) = 35 above gcd(w) = 8
+    (dict(dtype=_native.DA_F32), -4), (dict(dtype=2), -4), (dict(Dh=32), -5),
+    (dict(q=Q + 8), -7), (dict(lse=LSE + 2), -7),
+    (dict(out=Q), -8), (dict(lse=K + 64), -8), (dict(out=LSE), -8),
+    (dict(causal=2), -9), (dict(scale=math.nan), -9),
+])
+def test_onepass_invalid_calls_rejected(lib, kwargs, code):
+    assert onepass(lib, **kwargs) == code
+
+
+def test_onepass_empty_problem_is_a_no_op(lib):
+    assert onepass(lib, B=0, q=None, k=None, v=None, out=None, lse=None) == 0
