@@ -231,15 +231,21 @@ int dilated_attn_qk_norm_bwd(const void* xq, const void* xk, const void* dyq, co
  * DA_ERR_PATTERN; the separate dilated_attn_qk_norm_* and dilated_attn_*
  * calls compute the same values there.
  *
- * xq, xk, v as q, k, v of dilated_attn_fwd (the un-normalised rows); gains
- * and biases Dh values of dtype, 16-byte aligned, not overlapping any
+ * xq, xk, v as q, k, v of dilated_attn_fwd (the un-normalised rows), except
+ * that row_stride gives the elements between consecutive positions of each
+ * (0: H * Dh, the dense [B, N, H, Dh] layout; otherwise at least H * Dh, the
+ * rows 16-byte aligned, DA_ERR_ARG / DA_ERR_ALIGN): xq, xk, v may then be
+ * the three parts of one [B, N, 3, H, Dh] buffer, as one projection GEMM
+ * writes them (row_stride 3 H Dh). out and lse keep their dense layouts.
+ * Gains and biases: Dh values of dtype, 16-byte aligned, not overlapping any
  * output; eps finite and > 0 (DA_ERR_ARG). No workspace. Other arguments,
  * checks and outputs as dilated_attn_fwd. */
 int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
                             const void* bias_q, const void* gain_k, const void* bias_k,
                             float eps, void* out, float* lse, int64_t B, int64_t N, int32_t H,
-                            int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
-                            int32_t causal, int32_t dtype, float scale, void* stream);
+                            int32_t Dh, int64_t row_stride, const da_pattern* patterns,
+                            int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                            void* stream);
 
 /* Device workspace bytes of dilated_attn_bwd_qknorm (the backward's own,
  * plus per-(batch, head, segment) partial sums of the gain and bias
@@ -249,7 +255,9 @@ int dilated_attn_bwd_qknorm_workspace_bytes(int64_t B, int64_t N, int32_t H, int
                                             int32_t dtype, size_t* bytes);
 
 /* Backward of dilated_attn_fwd_qknorm: dxq, dxk (gradients with respect to
- * the un-normalised rows, [B, N, H, Dh] of dtype), dv, and dparams, a device
+ * the un-normalised rows, of dtype), dv, all three in the layout row_stride
+ * gives xq, xk, v (they may interleave in one buffer; rows of one must not
+ * touch rows of another, DA_ERR_ALIAS), and dparams, a device
  * float array [2][2][Dh] as for dilated_attn_qk_norm_bwd (gain_q, bias_q,
  * gain_k, bias_k gradients), all written. out and lse as dilated_attn_fwd_qknorm
  * returned them. The gain and bias gradients are summed in a fixed order
@@ -259,7 +267,7 @@ int dilated_attn_bwd_qknorm(const void* xq, const void* xk, const void* v, const
                             const void* bias_q, const void* gain_k, const void* bias_k,
                             float eps, const void* out, const float* lse, const void* dout,
                             void* dxq, void* dxk, void* dv, float* dparams, int64_t B, int64_t N,
-                            int32_t H, int32_t Dh, const da_pattern* patterns,
+                            int32_t H, int32_t Dh, int64_t row_stride, const da_pattern* patterns,
                             int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
 

@@ -299,40 +299,60 @@ def _check_out(name, t, shape, dtype, device):
                          f"on {device}")
 
 
+def _row_stride(named):
+    """Common stride (elements) between consecutive positions of [B, N, H,
+    Dh] tensors whose [H, Dh] rows are dense, e.g. the three parts
+    qkv[:, :, i] of one [B, N, 3, H, Dh] buffer; 0 when they are dense."""
+    rs = None
+    for name, t in named:
+        B, N, H, Dh = t.shape
+        ok = t.stride(3) == 1 and t.stride(2) == Dh and (B == 1 or t.stride(0) == N * t.stride(1))
+        if not ok or (rs is not None and t.stride(1) != rs):
+            raise ValueError(f"{name} must be [B, N, H, Dh] with dense [H, Dh] rows at one common "
+                             "stride between positions (e.g. contiguous, or a part of a "
+                             "[B, N, 3, H, Dh] buffer)")
+        rs = t.stride(1)
+    B, N, H, Dh = named[0][1].shape
+    return 0 if rs == H * Dh else int(rs)
+
+
 def _check_fused(xq, xk, v, params):
     import torch
 
     for name, t in (("xq", xq), ("xk", xk), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
             raise ValueError(f"{name} must be a GPU tensor; no CPU path exists")
-        if t.dim() != 4 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous [B, N, H, Dh] tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be a [B, N, H, Dh] tensor")
         if t.shape != xq.shape or t.dtype != xq.dtype or t.device != xq.device:
             raise ValueError(f"{name} must match xq in shape, dtype and device")
     for name, t in zip(("gain_q", "bias_q", "gain_k", "bias_k"), params):
         _check_rows(name, t, xq)
         if t.numel() != DA_HEAD_DIM:
             raise ValueError(f"{name} must hold {DA_HEAD_DIM} values")
+    return _row_stride((("xq", xq), ("xk", xk), ("v", v)))
 
 
 def dilated_attn_qknorm(xq, xk, v, gain_q, bias_q, gain_k, bias_k, patterns, eps=1e-5,
                         causal=True, scale=None, out=None, lse=None):
     """Forward of attention over qk_norm(xq), qk_norm(xk), v with the layer
     norm applied inside the attention kernel. Returns (out, lse); one pattern
-    with segments of at most 32 gathered rows (see qknorm_fused_supported)."""
+    with segments of at most 32 gathered rows (see qknorm_fused_supported).
+    xq, xk, v may be the parts qkv[:, :, 0..2] of one [B, N, 3, H, Dh]
+    buffer; out is a dense [B, N, H, Dh] tensor."""
     import torch
 
     params = (gain_q, bias_q, gain_k, bias_k)
-    _check_fused(xq, xk, v, params)
+    rs = _check_fused(xq, xk, v, params)
     B, N, H, Dh = (int(x) for x in xq.shape)
     pats = [(int(w), int(r)) for (w, r) in patterns]
-    out = torch.empty_like(xq) if out is None else out
+    out = torch.empty((B, N, H, Dh), dtype=xq.dtype, device=xq.device) if out is None else out
     lse = torch.empty((B, H, N), dtype=torch.float32, device=xq.device) if lse is None else lse
     _check_out("out", out, xq.shape, xq.dtype, xq.device)
     _check_out("lse", lse, (B, H, N), torch.float32, xq.device)
     code = load_library().dilated_attn_fwd_qknorm(
         xq.data_ptr(), xk.data_ptr(), v.data_ptr(), *(t.data_ptr() for t in params), float(eps),
-        out.data_ptr(), lse.data_ptr(), B, N, H, Dh, _native.pattern_array(pats), len(pats),
+        out.data_ptr(), lse.data_ptr(), B, N, H, Dh, rs, _native.pattern_array(pats), len(pats),
         1 if causal else 0, _dtype_code(xq), float(scale) if scale else 0.0,
         torch.cuda.current_stream(xq.device).cuda_stream)
     _native.check(code, "dilated_attn_fwd_qknorm")
@@ -343,12 +363,13 @@ def dilated_attn_qknorm_bwd(xq, xk, v, gain_q, bias_q, gain_k, bias_k, out, lse,
                             eps=1e-5, causal=True, scale=None, workspace=None, dxq=None,
                             dxk=None, dv=None, dparams=None):
     """Backward of dilated_attn_qknorm. Returns (dxq, dxk, dv, dparams), with
-    dparams a float32 [2, 2, 64] tensor: [q|k][gain|bias]; outputs are
-    allocated unless given."""
+    dparams a float32 [2, 2, 64] tensor: [q|k][gain|bias]. dxq, dxk, dv take
+    the layout of xq, xk, v (given ones must match it; allocated ones are
+    parts of one [B, N, 3, H, Dh] buffer when xq, xk, v are)."""
     import torch
 
     params = (gain_q, bias_q, gain_k, bias_k)
-    _check_fused(xq, xk, v, params)
+    rs = _check_fused(xq, xk, v, params)
     for name, t in (("out", out), ("dout", dout)):
         if not isinstance(t, torch.Tensor) or t.shape != xq.shape or t.dtype != xq.dtype \
                 or t.device != xq.device or not t.is_contiguous():
@@ -362,19 +383,34 @@ def dilated_attn_qknorm_bwd(xq, xk, v, gain_q, bias_q, gain_k, bias_k, out, lse,
     if workspace is None:
         ws = _native.bwd_qknorm_workspace_bytes(B, N, H, Dh, pats, dt)
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=xq.device)
-    dxq = torch.empty_like(xq) if dxq is None else dxq
-    dxk = torch.empty_like(xk) if dxk is None else dxk
-    dv = torch.empty_like(v) if dv is None else dv
+    if dxq is None and dxk is None and dv is None:
+        if rs == 0:
+            dxq, dxk, dv = (torch.empty((B, N, H, Dh), dtype=xq.dtype, device=xq.device)
+                            for _ in range(3))
+        else:
+            if rs >= 3 * H * Dh:  # one buffer, the three interleaved
+                g = torch.empty((B, N, rs), dtype=xq.dtype, device=xq.device)
+                dxq, dxk, dv = (g[:, :, i * H * Dh:(i + 1) * H * Dh].unflatten(2, (H, Dh))
+                                for i in range(3))
+            else:  # three buffers of that layout
+                dxq, dxk, dv = (torch.empty((B, N, rs), dtype=xq.dtype, device=xq.device)
+                                [:, :, :H * Dh].unflatten(2, (H, Dh)) for _ in range(3))
+    if dxq is None or dxk is None or dv is None:
+        raise ValueError("give all of dxq, dxk, dv or none")
+    for name, t in (("dxq", dxq), ("dxk", dxk), ("dv", dv)):
+        if (not isinstance(t, torch.Tensor) or t.shape != xq.shape or t.dtype != xq.dtype
+                or t.device != xq.device):
+            raise ValueError(f"{name} must be a tensor like xq")
+    if _row_stride((("dxq", dxq), ("dxk", dxk), ("dv", dv))) != rs:
+        raise ValueError("dxq, dxk, dv must have the layout of xq, xk, v")
     if dparams is None:
         dparams = torch.empty((2, 2, DA_HEAD_DIM), dtype=torch.float32, device=xq.device)
-    for name, t in (("dxq", dxq), ("dxk", dxk), ("dv", dv)):
-        _check_out(name, t, xq.shape, xq.dtype, xq.device)
     _check_out("dparams", dparams, (2, 2, DA_HEAD_DIM), torch.float32, xq.device)
     code = load_library().dilated_attn_bwd_qknorm(
         xq.data_ptr(), xk.data_ptr(), v.data_ptr(), *(t.data_ptr() for t in params), float(eps),
         out.data_ptr(), lse.data_ptr(), dout.data_ptr(), dxq.data_ptr(), dxk.data_ptr(),
-        dv.data_ptr(), dparams.data_ptr(), B, N, H, Dh, _native.pattern_array(pats), len(pats),
-        1 if causal else 0, dt, float(scale) if scale else 0.0, workspace.data_ptr(),
+        dv.data_ptr(), dparams.data_ptr(), B, N, H, Dh, rs, _native.pattern_array(pats),
+        len(pats), 1 if causal else 0, dt, float(scale) if scale else 0.0, workspace.data_ptr(),
         workspace.numel() * workspace.element_size(),
         torch.cuda.current_stream(xq.device).cuda_stream)
     _native.check(code, "dilated_attn_bwd_qknorm")

@@ -180,6 +180,45 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// A buffer's bytes for the alias checks: a dense range, or rows of `row`
+// bytes every `stride` bytes (tensors that interleave in one buffer).
+struct Region {
+  const void* p;
+  size_t bytes;       // first to last byte touched
+  size_t stride = 0;  // 0: every byte of the range
+  size_t row = 0;
+};
+Region dense(const void* p, size_t bytes) { return Region{p, bytes, 0, 0}; }
+Region rows_of(const void* p, int64_t rows, size_t stride, size_t row) {
+  return Region{p, rows > 0 ? (size_t)(rows - 1) * stride + row : 0, stride, row};
+}
+// Whether two regions may share a byte: two row sets with the same stride
+// and row size are apart when their offset, modulo the stride, keeps every
+// row of one between rows of the other.
+bool collide(const Region& a, const Region& b) {
+  if (!overlaps(a.p, a.bytes, b.p, b.bytes)) return false;
+  if (a.stride && a.stride == b.stride && a.row == b.row && a.stride >= 2 * a.row) {
+    const int64_t st = (int64_t)a.stride;
+    const int64_t d = (((int64_t)((uintptr_t)b.p - (uintptr_t)a.p)) % st + st) % st;
+    return d < (int64_t)a.row || d > st - (int64_t)a.row;
+  }
+  return true;
+}
+
+// Row stride (elements between consecutive positions) of the fused qk_norm
+// entry points' q, k, v (and dq, dk, dv): 0 means H * Dh.
+int qkn_row_stride(const Plan& pl, int64_t given, int64_t* rsi) {
+  const int64_t hd = (int64_t)pl.H * DA_HEAD_DIM;
+  const int64_t es = pl.bf16 ? 2 : 4;
+  *rsi = given == 0 ? hd : given;
+  if (given < 0 || (given != 0 && given < hd)) return DA_ERR_ARG;
+  if ((*rsi * es) % 16 != 0) return DA_ERR_ALIGN;
+  // the kernels address one segment's rows with 32-bit byte offsets
+  for (int i = 0; i < pl.np; ++i)
+    if ((pl.pat[i].wp + 128 * (int64_t)pl.pat[i].r) * *rsi * es > kMaxGrid) return DA_ERR_SHAPE;
+  return DA_OK;
+}
+
 int check_buffers(const Plan& pl, const void* q, const void* k, const void* v, const void* out,
                   const float* lse, const void* ws, size_t ws_bytes) {
   if (!q || !k || !v || !out || !lse) return DA_ERR_NULL;
@@ -201,7 +240,7 @@ int check_buffers(const Plan& pl, const void* q, const void* k, const void* v, c
 // qkn: gain_q, bias_q, gain_k, bias_k of the fused qk_norm, or null
 int run_attention(const Plan& pl, const void* q, const void* k, const void* v, void* out,
                   float* lse, void* ws, hipStream_t st, const void* const* qkn = nullptr,
-                  float qkn_eps = 0.f) {
+                  float qkn_eps = 0.f, int64_t in_rs = 0) {
   da::AttnArgs a;
   memset(&a, 0, sizeof a);
   a.q = q;
@@ -217,6 +256,7 @@ int run_attention(const Plan& pl, const void* q, const void* k, const void* v, v
   a.sl2 = pl.sl2;
   sorted_patterns(pl, pl.fwd, a.pat, a.unit_start);
   hipError_t e;
+  a.in_rs = in_rs ? in_rs : (int64_t)pl.H * DA_HEAD_DIM;
   if (qkn) {
     for (int i = 0; i < 4; ++i) a.qkn[i] = qkn[i];
     a.qkn_eps = qkn_eps;
@@ -325,11 +365,12 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
                int64_t N, int32_t H, int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
                int32_t causal, int32_t dtype, float scale, void* workspace,
                size_t workspace_bytes, void* stream, const void* const* qkn = nullptr,
-               float qkn_eps = 0.f, float* dparams = nullptr) {
+               float qkn_eps = 0.f, float* dparams = nullptr, int64_t row_stride = 0) {
   if (stages < 1 || stages > DA_BWD_ALL) return DA_ERR_ARG;
   Plan pl;
   int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
   if (rc != DA_OK) return rc;
+  int64_t rsi = (int64_t)pl.H * DA_HEAD_DIM;
   if (qkn) {
     const void* outs[4] = {dq, dk, dv, dparams};
     const size_t ob[4] = {pl.tensor_bytes, pl.tensor_bytes, pl.tensor_bytes,
@@ -351,12 +392,38 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
     for (int j = 0; j < 3; ++j)
       if (overlaps(dparams, pb, outs[j], pl.tensor_bytes)) return DA_ERR_ALIAS;
     if (overlaps(dparams, pb, workspace, qkn_bwd_ws_bytes(pl))) return DA_ERR_ALIAS;
+    rc = qkn_row_stride(pl, row_stride, &rsi);
+    if (rc != DA_OK) return rc;
   }
   if (pl.empty) return DA_OK;
   Plan chk = pl;  // the fused qk_norm backward needs room for its partials
   if (qkn) chk.bwd_ws_bytes = qkn_bwd_ws_bytes(pl);
-  rc = check_bwd_buffers(chk, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes);
-  if (rc != DA_OK) return rc;
+  if (qkn && rsi != (int64_t)pl.H * DA_HEAD_DIM) {
+    // q, k, v and dq, dk, dv as rows every rsi elements (they may interleave)
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return DA_ERR_NULL;
+    if (!workspace || workspace_bytes < chk.bwd_ws_bytes) return DA_ERR_WORKSPACE;
+    auto mis = [](const void* p, uintptr_t al) { return ((uintptr_t)p & (al - 1)) != 0; };
+    const void* t16[8] = {q, k, v, out, dout, dq, dk, dv};
+    for (const void* t : t16)
+      if (mis(t, 16)) return DA_ERR_ALIGN;
+    if (mis(lse, 4) || mis(workspace, 256)) return DA_ERR_ALIGN;
+    const int64_t es = pl.bf16 ? 2 : 4, rows = pl.B * pl.N;
+    const size_t rb = (size_t)(rsi * es), row = (size_t)(pl.H * DA_HEAD_DIM * es);
+    const Region ins[6] = {rows_of(q, rows, rb, row),       rows_of(k, rows, rb, row),
+                           rows_of(v, rows, rb, row),       dense(out, pl.tensor_bytes),
+                           dense(dout, pl.tensor_bytes),    dense(lse, pl.lse_bytes)};
+    const Region outs[4] = {rows_of(dq, rows, rb, row), rows_of(dk, rows, rb, row),
+                            rows_of(dv, rows, rb, row), dense(workspace, chk.bwd_ws_bytes)};
+    for (int i = 0; i < 4; ++i) {
+      for (int j = 0; j < 6; ++j)
+        if (collide(outs[i], ins[j])) return DA_ERR_ALIAS;
+      for (int j = i + 1; j < 4; ++j)
+        if (collide(outs[i], outs[j])) return DA_ERR_ALIAS;
+    }
+  } else {
+    rc = check_bwd_buffers(chk, q, k, v, out, lse, dout, dq, dk, dv, workspace, workspace_bytes);
+    if (rc != DA_OK) return rc;
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   float* ws = reinterpret_cast<float*>(workspace);
 
@@ -373,6 +440,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   ra.N = pl.N;
   ra.H = pl.H;
   ra.np = pl.np;
+  ra.grad_rs = rsi;
   for (int i = 0; i < pl.np; ++i) {
     ra.pat[i] = pl.pat[i];
     ra.pat[i].po_off = pl.bwd_po_off[i];
@@ -401,6 +469,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   for (int j = 0; j < pl.np; ++j) a.pat[j].po_off = pl.bwd_po_off[pl.bwd.order[j]];
   float* const qkn_part =
       reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + qkn_part_offset(pl));
+  a.in_rs = rsi;
   if (qkn) {
     for (int i = 0; i < 4; ++i) a.qkn[i] = qkn[i];
     a.qkn_eps = qkn_eps;
@@ -540,8 +609,9 @@ int dilated_attn_fwd_onepass(const void* q, const void* k, const void* v, void* 
 int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,
                             const void* bias_q, const void* gain_k, const void* bias_k,
                             float eps, void* out, float* lse, int64_t B, int64_t N, int32_t H,
-                            int32_t Dh, const da_pattern* patterns, int32_t n_patterns,
-                            int32_t causal, int32_t dtype, float scale, void* stream) {
+                            int32_t Dh, int64_t row_stride, const da_pattern* patterns,
+                            int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
+                            void* stream) {
   Plan pl;
   int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
   if (rc != DA_OK) return rc;
@@ -550,10 +620,29 @@ int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const
   const size_t ob[2] = {pl.tensor_bytes, pl.lse_bytes};
   rc = qkn_params_check(pl, gb, eps, outs, ob, 2);
   if (rc != DA_OK || pl.empty) return rc;
-  rc = check_buffers(pl, xq, xk, v, out, lse, nullptr, 0);
+  int64_t rsi = 0;
+  rc = qkn_row_stride(pl, row_stride, &rsi);
+  if (rc != DA_OK) return rc;
+  if (rsi == (int64_t)pl.H * DA_HEAD_DIM) {
+    rc = check_buffers(pl, xq, xk, v, out, lse, nullptr, 0);
+  } else {
+    if (!xq || !xk || !v || !out || !lse) return DA_ERR_NULL;
+    auto mis = [](const void* p, uintptr_t al) { return ((uintptr_t)p & (al - 1)) != 0; };
+    if (mis(xq, 16) || mis(xk, 16) || mis(v, 16) || mis(out, 16) || mis(lse, 4))
+      return DA_ERR_ALIGN;
+    const int64_t es = pl.bf16 ? 2 : 4, rows = pl.B * pl.N;
+    const size_t rb = (size_t)(rsi * es), row = (size_t)(pl.H * DA_HEAD_DIM * es);
+    const Region ins[3] = {rows_of(xq, rows, rb, row), rows_of(xk, rows, rb, row),
+                           rows_of(v, rows, rb, row)};
+    const Region o[2] = {dense(out, pl.tensor_bytes), dense(lse, pl.lse_bytes)};
+    for (const Region& x : o)
+      for (const Region& y : ins)
+        if (collide(x, y)) return DA_ERR_ALIAS;
+    if (collide(o[0], o[1])) return DA_ERR_ALIAS;
+  }
   if (rc != DA_OK) return rc;
   return run_attention(pl, xq, xk, v, out, lse, nullptr, reinterpret_cast<hipStream_t>(stream),
-                       gb, eps);
+                       gb, eps, rsi);
 }
 
 int dilated_attn_bwd_qknorm_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
@@ -576,13 +665,13 @@ int dilated_attn_bwd_qknorm(const void* xq, const void* xk, const void* v, const
                             const void* bias_q, const void* gain_k, const void* bias_k,
                             float eps, const void* out, const float* lse, const void* dout,
                             void* dxq, void* dxk, void* dv, float* dparams, int64_t B, int64_t N,
-                            int32_t H, int32_t Dh, const da_pattern* patterns,
+                            int32_t H, int32_t Dh, int64_t row_stride, const da_pattern* patterns,
                             int32_t n_patterns, int32_t causal, int32_t dtype, float scale,
                             void* workspace, size_t workspace_bytes, void* stream) {
   const void* gb[4] = {gain_q, bias_q, gain_k, bias_k};
   return bwd_common(DA_BWD_ALL, xq, xk, v, out, lse, dout, dxq, dxk, dv, B, N, H, Dh, patterns,
                     n_patterns, causal, dtype, scale, workspace, workspace_bytes, stream, gb, eps,
-                    dparams);
+                    dparams, row_stride);
 }
 
 int dilated_attn_fwd_attention(const void* q, const void* k, const void* v, void* out, float* lse,

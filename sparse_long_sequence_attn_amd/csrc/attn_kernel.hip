@@ -206,9 +206,13 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   const int64_t rs = (int64_t)a.H * kDh;  // elements between consecutive positions
   const int64_t seg0 = tl.seg * wp;
   const int64_t headbase = tl.b * a.N * rs + (int64_t)tl.h * kDh;
+  // q, k, v rows: the output's layout, or with qk_norm fused a caller-given
+  // position stride (q, k, v may interleave in one buffer)
+  const int64_t rsi = QKN ? a.in_rs : rs;
   // gathered row m starts at element rowbase + m * mstride
-  const int64_t rowbase = headbase + gathered_pos(tl.seg, wp, off, r, 0) * rs;
-  const int64_t mstride = (int64_t)r * rs;
+  const int64_t rowbase =
+      tl.b * a.N * rsi + (int64_t)tl.h * kDh + gathered_pos(tl.seg, wp, off, r, 0) * rsi;
+  const int64_t mstride = (int64_t)r * rsi;
 
   const int32_t qend_wg = min(L, q0 + BM);
   const int32_t nkt = CAUSAL ? (qend_wg + BN - 1) / BN : (L + BN - 1) / BN;

@@ -907,21 +907,38 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int64_t rowbase = g.headbase + (g.seg0 + g.off) * g.rs;
-  const auto rq = dev_rsrc(reinterpret_cast<const T*>(a.q) + rowbase, g.range);
-  const auto rk = dev_rsrc(reinterpret_cast<const T*>(a.k) + rowbase, g.range);
-  const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, g.range);
+  // q, k, v and dq, dk, dv: with qk_norm fused a caller-given position
+  // stride (they may interleave in one buffer); out and dout as the output
+  const int64_t rsi = QKN ? a.in_rs : g.rs;
+  const int64_t headbase_in = QKN ? tl.b * a.N * rsi + (int64_t)tl.h * kDh : g.headbase;
+  const int64_t rowbase_in = headbase_in + (g.seg0 + g.off) * rsi;
+  const uint32_t mbytes_in = QKN ? (uint32_t)((int64_t)g.r * rsi * (int64_t)sizeof(T)) : g.mbytes;
+  const uint32_t range_in =
+      QKN ? (uint32_t)(g.L - 1) * mbytes_in + (uint32_t)(kDh * sizeof(T)) : g.range;
+  const auto rq = dev_rsrc(reinterpret_cast<const T*>(a.q) + rowbase_in, range_in);
+  const auto rk = dev_rsrc(reinterpret_cast<const T*>(a.k) + rowbase_in, range_in);
+  const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase_in, range_in);
   const auto rdo = dev_rsrc(reinterpret_cast<const T*>(a.dout) + rowbase, g.range);
   const auto ro = dev_rsrc(reinterpret_cast<const T*>(a.out) + rowbase, g.range);
 
-  // rows past L load as zeros: D = 0 there, and lse2 = +inf makes P = 0
+  // rows past L load as zeros: D = 0 there, and lse2 = +inf makes P = 0.
+  // Pairs with one row stride each: (q, dout) and (k, out), or with qk_norm
+  // (q, k) and (dout, out).
   using Stg = PairStager<BF, 32, 64>;
-  Stg sqd, sko;
-  sqd.init(lane, g.mbytes);
-  sko.init(lane, g.mbytes);
-  sqd.load(rq, rdo, 0);
-  sko.load(rk, ro, 0);
+  Stg s1, s2;
+  if constexpr (QKN) {
+    s1.init(lane, mbytes_in);
+    s2.init(lane, g.mbytes);
+    s1.load(rq, rk, 0);
+    s2.load(rdo, ro, 0);
+  } else {
+    s1.init(lane, g.mbytes);
+    s2.init(lane, g.mbytes);
+    s1.load(rq, rdo, 0);
+    s2.load(rk, ro, 0);
+  }
   RowFrag<BF> vf;  // B operand of dP = dout V^T
-  vf.load(rv, (uint32_t)n * g.mbytes, hh);
+  vf.load(rv, (uint32_t)n * mbytes_in, hh);
   int64_t pos = 0;
   float l2 = INFINITY;
   if (n < g.L) {
@@ -936,7 +953,7 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t o = sko.rb[i][e], d = sqd.rb[i][e];
+      const uint32_t o = s2.rb[i][e], d = QKN ? s2.ra[i][e] : s1.rb[i][e];
       if constexpr (BF) {
         s = fmaf(__uint_as_float(o << 16), __uint_as_float(d << 16), s);
         s = fmaf(__uint_as_float(o & 0xffff0000u), __uint_as_float(d & 0xffff0000u), s);
@@ -949,11 +966,14 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
     if (lane % CPR == 0) dd[(lane + 64 * i) / CPR] = s;
   }
   if constexpr (QKN) {
-    qkn_normalize<BF>(sqd.ra, a.qkn[0], a.qkn[1], a.qkn_eps, g.L, lane, qst, qst + 32);
-    qkn_normalize<BF>(sko.ra, a.qkn[2], a.qkn[3], a.qkn_eps, g.L, lane, qst + 64, qst + 96);
+    qkn_normalize<BF>(s1.ra, a.qkn[0], a.qkn[1], a.qkn_eps, g.L, lane, qst, qst + 32);
+    qkn_normalize<BF>(s1.rb, a.qkn[2], a.qkn[3], a.qkn_eps, g.L, lane, qst + 64, qst + 96);
+    s1.store(lane, Qs, Ks);
+    s2.store_first(lane, Ds);
+  } else {
+    s1.store(lane, Qs, Ds);
+    s2.store_first(lane, Ks);
   }
-  sqd.store(lane, Qs, Ds);
-  sko.store_first(lane, Ks);
   if (hh == 0) ls[n] = l2;
   __syncthreads();
 
@@ -1068,7 +1088,7 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
       }
   }
   XRow<BF> xq[QKN ? 8 : 1];  // QKN: q's input rows for the dq epilogue
-  if constexpr (QKN) load_rows_x<BF>(xq, rq, g.mbytes, lane);
+  if constexpr (QKN) load_rows_x<BF>(xq, rq, mbytes_in, lane);
   __syncthreads();  // tiles consumed: the staging area takes their place
 
   const PatDev& P = a.pat[tl.p];
@@ -1086,11 +1106,11 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
   float* const part = a.ws + P.po_off + prow0 * kDh;
   stage_row(srow, dQ, a.scale, n, hh);
   XRow<BF> xk[QKN ? 8 : 1];  // QKN: k's input rows for the dk epilogue
-  if constexpr (QKN) load_rows_x<BF>(xk, rk, g.mbytes, lane);
+  if constexpr (QKN) load_rows_x<BF>(xk, rk, mbytes_in, lane);
   __syncthreads();
   if constexpr (QKN) {
     const int64_t unit = prow0 / P.lmax;
-    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, xq,
+    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + headbase_in, rsi, xq,
                        qst, qst + 32, a.qkn[0], a.qkn_part + unit * 2 * kDh, lane);
   } else {
     write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dq) + g.headbase, g.rs, part, lane);
@@ -1100,7 +1120,7 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
   __syncthreads();
   if constexpr (QKN) {
     const int64_t unit = prow0 / P.lmax;
-    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + g.headbase, g.rs, xk,
+    write_rows_qkn<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dk) + headbase_in, rsi, xk,
                        qst + 64, qst + 96, a.qkn[2], a.qkn_part + (a.qkn_units + unit) * 2 * kDh,
                        lane);
   } else {
@@ -1110,7 +1130,7 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
   __syncthreads();
   stage_row(srow, dV, 1.f, n, hh);
   __syncthreads();
-  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dv) + g.headbase, g.rs,
+  write_rows<BF>(srow, mpos, mkind, reinterpret_cast<T*>(a.dv) + headbase_in, rsi,
                  part + 2 * slots * kDh, lane);
 }
 
@@ -1209,7 +1229,7 @@ __global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs
   }
   if (cover == 1) return;
 
-  const int64_t elem = ((b * a.N + t) * a.H + h) * kDh + kDimsPerLane * sub;
+  const int64_t elem = (b * a.N + t) * a.grad_rs + (int64_t)h * kDh + kDimsPerLane * sub;
   void* const dst[3] = {a.dq, a.dk, a.dv};
 #pragma unroll
   for (int w = 0; w < 3; ++w) {

@@ -41,6 +41,10 @@ struct BwdArgs {
   float qkn_eps;
   float* qkn_part;
   int64_t qkn_units;
+  // qk_norm fused: elements between consecutive positions of q, k, v and
+  // of dq, dk, dv (at least H * Dh; they may interleave); out and dout stay
+  // [B, N, H, Dh]
+  int64_t in_rs;
   PatDev pat[kMaxPat];
   int64_t unit_start[kMaxPat + 1];
 };
@@ -59,6 +63,7 @@ struct BwdRowArgs {
   int64_t N;
   int32_t H;
   int32_t np;
+  int64_t grad_rs;  // elements between consecutive positions of dq, dk, dv
   PatDev pat[kMaxPat];  // caller's order
 };
 

@@ -81,6 +81,9 @@ struct AttnArgs {
   // qk_norm fused: gain_q, bias_q, gain_k, bias_k (Dh values each, q's dtype);
   // q and k then hold the un-normalised rows
   const void* qkn[4];
+  // qk_norm fused: elements between consecutive positions of q, k and v (at
+  // least H * Dh; they may interleave in one buffer); out stays [B, N, H, Dh]
+  int64_t in_rs;
   PatDev pat[kMaxPat];
   int64_t unit_start[kMaxPat + 1];  // first global unit of each sorted pattern
 };

@@ -16,7 +16,9 @@ kernels where the library supports it (one pattern whose segments gather at
 most 32 rows, as in the README's usage example): q and k are normalised as
 the kernels load them and never stored, and the backward kernel turns the
 attention gradients into gradients of the un-normalised rows and of the
-gains and biases. Elsewhere it runs in this library's layer-norm kernels
+gains and biases. There q, k and v come from one GEMM as one [B, N, 3,
+heads, 64] tensor, which the kernels read in place, and their gradients go
+back through one GEMM the same way. Elsewhere it runs in this library's layer-norm kernels
 (both tensors in one launch each way) before the attention.
 """
 from typing import Optional, Sequence, Tuple, Union
@@ -71,23 +73,28 @@ class QKNormFunction(torch.autograd.Function):
 class QKNormAttnFunction(torch.autograd.Function):
     """out = dilated attention(qk_norm(xq), qk_norm(xk), v) with the layer
     norm inside the attention kernels; the normalised q and k never exist in
-    memory."""
+    memory. xq, xk, v are the parts of one [B, N, 3, H, 64] tensor (one
+    projection GEMM writes them) and its gradient comes back in that layout
+    (one GEMM takes it)."""
 
     @staticmethod
-    def forward(ctx, xq, xk, v, gq, bq, gk, bk, eps, patterns, causal, scale):
+    def forward(ctx, qkv, gq, bq, gk, bk, eps, patterns, causal, scale):
+        xq, xk, v = qkv.unbind(2)
         out, lse = dilated_attn_qknorm(xq, xk, v, gq, bq, gk, bk, patterns, eps, causal, scale)
-        ctx.save_for_backward(xq, xk, v, gq, bq, gk, bk, out, lse)
+        ctx.save_for_backward(qkv, gq, bq, gk, bk, out, lse)
         ctx.eps, ctx.patterns, ctx.causal, ctx.scale = eps, patterns, causal, scale
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        xq, xk, v, gq, bq, gk, bk, out, lse = ctx.saved_tensors
-        dxq, dxk, dv, dp = dilated_attn_qknorm_bwd(xq, xk, v, gq, bq, gk, bk, out, lse,
-                                                   dout.contiguous(), ctx.patterns, ctx.eps,
-                                                   ctx.causal, ctx.scale)
+        qkv, gq, bq, gk, bk, out, lse = ctx.saved_tensors
+        dqkv = torch.empty_like(qkv)
+        dxq, dxk, dv = dqkv.unbind(2)
+        _, _, _, dp = dilated_attn_qknorm_bwd(*qkv.unbind(2), gq, bq, gk, bk, out, lse,
+                                              dout.contiguous(), ctx.patterns, ctx.eps,
+                                              ctx.causal, ctx.scale, dxq=dxq, dxk=dxk, dv=dv)
         dp = dp.to(gq.dtype)
-        return (dxq, dxk, dv, dp[0, 0], dp[0, 1], dp[1, 0], dp[1, 1], None, None, None, None)
+        return dqkv, dp[0, 0], dp[0, 1], dp[1, 0], dp[1, 1], None, None, None, None
 
 
 def _weight_grad(dy2, x2):
@@ -129,6 +136,43 @@ class ProjectionFunction(torch.autograd.Function):
             dws.append(_weight_grad(dy, x2))
             dbs.append(dy.sum(0) if hb else None)
         return (dx, None, *dws, *dbs)
+
+
+class PackedProjectionFunction(torch.autograd.Function):
+    """y = x [W_1; ...; W_n]^T (+ [b_1; ...; b_n]) as one GEMM for one input
+    x [R, in]: the n outputs side by side in y [R, n out]. The backward
+    takes dy in that layout: dx is one GEMM over K = n out, the weight
+    gradient one (row-split) GEMM, split back into the n weights."""
+
+    @staticmethod
+    def forward(ctx, x2, n, *wb):
+        ws, bs = wb[:n], wb[n:]
+        w = torch.cat(ws, 0)
+        b = torch.cat(bs, 0) if bs[0] is not None else None
+        ctx.save_for_backward(x2, w)
+        ctx.n, ctx.has_bias = n, bs[0] is not None
+        return torch.nn.functional.linear(x2, w, b)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x2, w = ctx.saved_tensors
+        dy = dy.contiguous()
+        dx = torch.mm(dy, w)
+        dws = _weight_grad(dy, x2).chunk(ctx.n, 0)
+        dbs = dy.sum(0).chunk(ctx.n, 0) if ctx.has_bias else (None,) * ctx.n
+        return (dx, None, *dws, *dbs)
+
+
+def _project_packed(x, layers):
+    """Apply nn.Linear layers that share the input x [..., in] (all with or
+    all without bias) as one GEMM; returns [..., n * out]."""
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    y = PackedProjectionFunction.apply(x2, len(layers), *[l.weight for l in layers],
+                                       *[l.bias for l in layers])
+    return y.view(*lead, y.shape[-1])
 
 
 def _project(x, layers):
@@ -205,12 +249,15 @@ class DilatedAttention(torch.nn.Module):
     def forward(self, x):
         B, N, _ = x.shape
         shape = (B, N, self.heads, self.HEAD_DIM)
-        q, k, v = (t.view(shape) for t in _project(x, [self.to_q, self.to_k, self.to_v]))
         if self._fused(x, B, N):
-            o = QKNormAttnFunction.apply(q, k, v, self.q_norm.weight, self.q_norm.bias,
+            # q, k, v from one GEMM, read by the attention kernels in place
+            qkv = _project_packed(x, [self.to_q, self.to_k, self.to_v])
+            o = QKNormAttnFunction.apply(qkv.view(B, N, 3, self.heads, self.HEAD_DIM),
+                                         self.q_norm.weight, self.q_norm.bias,
                                          self.k_norm.weight, self.k_norm.bias, self.q_norm.eps,
                                          self.patterns, self.causal, self.scale)
             return _project(o.view(B, N, self.dim), [self.to_out])[0]
+        q, k, v = (t.view(shape) for t in _project(x, [self.to_q, self.to_k, self.to_v]))
         if self.qk_norm:
             q, k = QKNormFunction.apply(q, k, self.q_norm.weight, self.q_norm.bias,
                                         self.k_norm.weight, self.k_norm.bias, self.q_norm.eps)

@@ -293,18 +293,18 @@ QKN_PATS = ((32, 2),)
 
 
 def fqkn_fwd(lib, xq=Q, xk=K, v=V, gq=GQ, bq=BQ, gk=GK, bk=BK, eps=1e-5, out=OUT, lse=LSE, B=1,
-             N=64, H=4, Dh=64, pats=QKN_PATS, causal=1, dtype=_native.DA_BF16, scale=0.0):
+             N=64, H=4, Dh=64, rs=0, pats=QKN_PATS, causal=1, dtype=_native.DA_BF16, scale=0.0):
     arr = _native.pattern_array(pats)
-    return lib.dilated_attn_fwd_qknorm(xq, xk, v, gq, bq, gk, bk, eps, out, lse, B, N, H, Dh, arr,
-                                       len(pats), causal, dtype, scale, None)
+    return lib.dilated_attn_fwd_qknorm(xq, xk, v, gq, bq, gk, bk, eps, out, lse, B, N, H, Dh, rs,
+                                       arr, len(pats), causal, dtype, scale, None)
 
 
 def fqkn_bwd(lib, xq=Q, xk=K, v=V, gq=GQ, bq=BQ, gk=GK, bk=BK, eps=1e-5, out=OUT, lse=LSE,
-             dout=DOUT, dxq=DQ, dxk=DK, dv=DV, dpar=DPAR, B=1, N=64, H=4, Dh=64, pats=QKN_PATS,
-             causal=1, dtype=_native.DA_BF16, scale=0.0, ws=WS, wsb=1 << 20):
+             dout=DOUT, dxq=DQ, dxk=DK, dv=DV, dpar=DPAR, B=1, N=64, H=4, Dh=64, rs=0,
+             pats=QKN_PATS, causal=1, dtype=_native.DA_BF16, scale=0.0, ws=WS, wsb=1 << 20):
     arr = _native.pattern_array(pats)
     return lib.dilated_attn_bwd_qknorm(xq, xk, v, gq, bq, gk, bk, eps, out, lse, dout, dxq, dxk,
-                                       dv, dpar, B, N, H, Dh, arr, len(pats), causal, dtype,
+                                       dv, dpar, B, N, H, Dh, rs, arr, len(pats), causal, dtype,
                                        scale, ws, wsb, None)
 
 
@@ -316,6 +316,8 @@ COMMON_FUSED_ERRORS = [
     (dict(dtype=2), -4), (dict(Dh=128), -5),
     (dict(gq=GQ + 8), -7), (dict(bk=BK + 4), -7),  # gains and biases: 16-byte aligned
     (dict(eps=0.0), -9), (dict(eps=math.nan), -9), (dict(causal=3), -9),
+    (dict(rs=-1), -9), (dict(rs=128), -9),   # below H * Dh = 256
+    (dict(rs=260), -7),                      # rows of 520 bytes: not 16-byte aligned
 ]
 
 
@@ -332,6 +334,12 @@ def test_fused_qknorm_fwd_invalid_calls_rejected(lib, kwargs, code):
     (dict(dpar=DPAR + 2), -7),
     (dict(dpar=Q), -8), (dict(dpar=DQ + 64), -8), (dict(dpar=WS + 256), -8),
     (dict(dxq=GK), -8), (dict(ws=GQ - 256), -8),
+    # q, k, v and their gradients as parts of one [B, N, 3, H, Dh] buffer
+    # (rows of 512 bytes every 1536): gradient rows on top of each other,
+    # or on the inputs, are aliases
+    (dict(rs=768, xk=Q + 512, v=Q + 1024, dxk=DQ + 64, dv=DQ + 1024), -8),
+    (dict(rs=768, xk=Q + 512, v=Q + 1024, dxq=Q + 1024, dxk=DQ + 512, dv=DQ + 1024), -8),
+    (dict(rs=768, xk=Q + 512, v=Q + 1024, dxk=DQ + 512, dv=DQ + 1024, ws=DQ + 4096), -8),
 ])
 def test_fused_qknorm_bwd_invalid_calls_rejected(lib, kwargs, code):
     assert fqkn_bwd(lib, **kwargs) == code

@@ -208,3 +208,37 @@ def test_fused_qknorm_rejects_other_patterns(torch_cuda):
         dilated_attn_qknorm(t["xq"], t["xk"], t["v"], t["gq"], t["bq"], t["gk"], t["bk"],
                             [(64, 2)], eps=0.0)
     assert e.value.code == -9
+
+
+@pytest.mark.parametrize("parts", [3, 4])
+@pytest.mark.parametrize("case", [(2, 256, 2, 64, 2, True, "bf16"), (1, 240, 3, 40, 3, False, "f32")],
+                         ids=["usage_pattern", "ragged"])
+def test_fused_qknorm_packed_layout(torch_cuda, case, parts):
+    """xq, xk, v as parts of one [B, N, parts, H, 64] buffer (row stride
+    parts * H * 64; parts = 3 is the module's one-GEMM layout): every output,
+    and the gradients written into such a buffer, equal the dense layout's
+    bit for bit (the kernels do the same arithmetic on the same values)."""
+    torch = torch_cuda
+    B, N, H, w, r, causal, dtype = case
+    pats = [(w, r)]
+    a = inputs(B, N, H, dtype, seed=980 + parts)
+    t = {n: to_torch(x) for n, x in a.items()}
+    dense = gpu_run(torch, a, pats, causal)
+    buf = torch.full((B, N, parts, H, 64), float("nan"), dtype=t["xq"].dtype, device="cuda")
+    for i, n in enumerate(("xq", "xk", "v")):
+        buf[:, :, i] = t[n]
+    xq, xk, v = buf[:, :, 0], buf[:, :, 1], buf[:, :, 2]
+    out, lse = dilated_attn_qknorm(xq, xk, v, t["gq"], t["bq"], t["gk"], t["bk"], pats, EPS,
+                                   causal)
+    gbuf = torch.full_like(buf, float("nan"))
+    dxq, dxk, dv, dpar = dilated_attn_qknorm_bwd(xq, xk, v, t["gq"], t["bq"], t["gk"], t["bk"],
+                                                 out, lse, t["dout"], pats, EPS, causal,
+                                                 dxq=gbuf[:, :, 0], dxk=gbuf[:, :, 1],
+                                                 dv=gbuf[:, :, 2])
+    torch.cuda.synchronize()
+    got = {"out": host(out), "lse": host(lse), "dxq": host(dxq), "dxk": host(dxk),
+           "dv": host(dv), "dparams": host(dpar)}
+    for n in got:
+        assert np.array_equal(got[n], dense[n], equal_nan=True), n
+    if parts == 4:  # the fourth part is no one's: untouched
+        assert torch.isnan(gbuf[:, :, 3]).all().item()
