@@ -300,7 +300,9 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
   constexpr int QBT = BQ / 32;
   constexpr int NT = 64 * NW;
   constexpr int ST = lds_stride<BF>();
-  constexpr int kTileElems = BQ * ST;
+  // bf16: Q and dout tiles loaded straight into LDS (128-byte rows, chunks
+  // at dma_slot); fp32: staged through registers into padded rows
+  constexpr int kTileElems = BF ? BQ * kDh : BQ * ST;
   constexpr int kTileBytes = kTileElems * (int)sizeof(T);
   constexpr int kBufBytes = 2 * kTileBytes + 2 * BQ * 4;  // Q, dout, lse2, D
   static_assert(kTileBytes % 16 == 0, "LDS alignment");
@@ -356,15 +358,26 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
   const int32_t qstart = CAUSAL ? k0 : 0;  // a multiple of BQ
   const int32_t nqt = (g.L - qstart + BQ - 1) / BQ;
 
-  PairStager<BF, BQ, NT> stg;
-  stg.init(tid, g.mbytes);
+  PairStager<BF, BF ? NT / 8 : BQ, NT> stg;  // fp32 only
+  DmaTile<BQ, NW> dmt;                      // bf16 only
+  if constexpr (BF)
+    dmt.init(wv, lane, g.mbytes);
+  else
+    stg.init(tid, g.mbytes);
   // lse and D of query row tid of the next tile; lse is scaled to log2 only
   // when stored, since using a loaded value right away would make the wave
-  // wait for the tile loads issued just before it
+  // wait for the tile loads issued just before it. bf16: the Q and dout
+  // tiles go into buffer buf directly.
   float lreg = 0.f, dreg = 0.f;
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t, int buf) {
     const int32_t m0 = qstart + t * BQ;
-    stg.load(rq, rdo, (uint32_t)m0 * g.mbytes);
+    if constexpr (BF) {
+      const lds_ptr qt = (lds_ptr)smem + buf * kBufBytes;
+      dmt.load(rq, qt, (uint32_t)m0 * g.mbytes, wv);
+      dmt.load(rdo, qt + kTileBytes, (uint32_t)m0 * g.mbytes, wv);
+    } else {
+      stg.load(rq, rdo, (uint32_t)m0 * g.mbytes);
+    }
     if (tid < BQ) {
       const int32_t m = m0 + tid;
       lreg = INFINITY;
@@ -378,7 +391,8 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
   };
   auto store_tile = [&](int buf) {
     char* base = smem + buf * kBufBytes;
-    stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
+    if constexpr (!BF)
+      stg.store(tid, reinterpret_cast<T*>(base), reinterpret_cast<T*>(base + kTileBytes));
     if (tid < BQ) {
       float* ls = reinterpret_cast<float*>(base + 2 * kTileBytes);
       ls[tid] = lreg * kLog2e;
@@ -387,7 +401,11 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
   };
 
   const float sl2 = a.sl2;
-  const uint32_t trl = tr_lane_offset<ST>(lane);
+  uint32_t trq[2][2];  // bf16: transpose-read offsets (dma_tr_offset)
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) trq[db][h] = BF ? dma_tr_offset(lane, h, db) : 0u;
 
   auto compute = [&](int buf, int t) {
     const char* base = smem + buf * kBufBytes;
@@ -407,8 +425,9 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
       if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + row * ST + 16 * ks + 8 * hh);
-          const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + row * ST + 16 * ks + 8 * hh);
+          const int oq = row * kDh + dma_slot(row, 2 * ks + hh) * 8;
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + oq);
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(Ds + oq);
           const int o = vrow * kDh + (((2 * ks + hh) ^ ((vrow >> 1) & 7)) << 3);
           const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Kl + o);
           S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, S, 0, 0, 0);
@@ -456,20 +475,32 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
       else
         probs(false);
       if constexpr (BF) {
-        const lds_cptr qbase = (lds_cptr)smem + buf * kBufBytes;
-        const lds_cptr dbase = qbase + kTileBytes;
+        const uint32_t qaddr = (uint32_t)reinterpret_cast<uintptr_t>((lds_ptr)smem) +
+                               (uint32_t)(buf * kBufBytes + qb * 32 * 128);
+        uint32_t ad[2][2], aq[2][2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            aq[db][h] = qaddr + trq[db][h];
+            ad[db][h] = aq[db][h] + kTileBytes;
+          }
+        bf16x8 dfr[2][2], qfr[2][2];  // dout^T, Q^T fragments [db][c]
+        dma_tr_read8(dfr, ad);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pk[c]);
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[db][c], pb, dV[db], 0, 0, 0);
+        }
+        dma_tr_read8(qfr, aq);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
           const bf16x8 sb = __builtin_bit_cast(bf16x8, sk[c]);
 #pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const uint32_t o = trl + (uint32_t)((qb * 32 + 16 * c) * ST + db * 32) * 2;
-            dV[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(dbase, o, ST), pb, dV[db],
-                                                             0, 0, 0);
-            dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment(qbase, o, ST), sb, dK[db],
-                                                             0, 0, 0);
-          }
+          for (int db = 0; db < 2; ++db)
+            dK[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfr[db][c], sb, dK[db], 0, 0, 0);
         }
       } else {
 #pragma unroll
@@ -486,14 +517,17 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
     }
   };
 
-  load_tile(0);
+  load_tile(0, 0);
   store_tile(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int t = 0; t < nqt; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nqt) load_tile(t + 1);
+    // the other buffer was last read before the previous barrier
+    if (t + 1 < nqt) load_tile(t + 1, buf ^ 1);
     compute(buf, t);
     if (t + 1 < nqt) store_tile(buf ^ 1);
+    if constexpr (BF) __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
     __syncthreads();
   }
 
