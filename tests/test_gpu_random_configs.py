@@ -1,0 +1,118 @@
+"""GPU parity on seeded random configurations: forward, backward and (bf16)
+the one-pass forward against the fp64 oracle, element by element, over
+pattern lists drawn at random — 1 to 4 patterns, segment lengths that
+divide N or exceed it, dilation rates that do and do not divide the segment,
+both causal settings, both dtypes, batch and head counts — at sizes the
+oracle finishes in well under a second each.
+
+Bars as in the other parity tests: out 1e-4 / 2e-2 (fp32 / bf16) absolute,
+lse 1e-4 / 4e-3 (test_gpu_parity.py derives them), gradients the same bar
+relative to each tensor's scale (test_gpu_bwd.py). Outputs are pre-filled
+with NaN; rows no pattern gathers must be exactly 0 / -inf / 0.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_long_sequence_attn_amd import (BwdProblem, DilatedAttnError, Problem,
+                                           dilated_attn_onepass)
+from sparse_long_sequence_attn_amd.workloads import grad_output, random_inputs, to_torch
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT = {"f32": 1e-4, "bf16": 2e-2}
+TOL_LSE = {"f32": 1e-4, "bf16": 4e-3}
+N_CASES = 24
+
+
+def draw_case(i):
+    """One configuration from its own PCG64 stream."""
+    rng = np.random.default_rng(5000 + i)
+    N = int(rng.choice([64, 96, 128, 192, 256, 384, 512]))
+    divisors = [d for d in range(2, N + 1) if N % d == 0]
+    pats = []
+    for _ in range(int(rng.integers(1, 5))):
+        u = rng.random()
+        if u < 0.35:  # long segments, small rates: the multi-wave kernels
+            w = int(rng.choice([N, N // 2] if N % 2 == 0 else [N]))
+            r = int(rng.integers(1, 4))
+        else:
+            w = int(rng.choice(divisors)) if u < 0.9 else N * int(rng.integers(2, 4))
+            r = int(rng.integers(1, min(min(w, N), 12) + 1))
+        pats.append((w, r))
+    return dict(B=int(rng.integers(1, 3)), N=N, H=int(rng.integers(1, 7)), patterns=pats,
+                causal=bool(rng.random() < 0.7), dtype="bf16" if rng.random() < 0.6 else "f32",
+                seed=6000 + i)
+
+
+CASES = [draw_case(i) for i in range(N_CASES)]
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check_fwd(out_g, lse_g, out_o, lse_o, dtype, label):
+    assert not np.isnan(out_g).any() and not np.isnan(lse_g).any(), f"{label}: unwritten"
+    fin = np.isfinite(lse_o)
+    assert np.array_equal(np.isfinite(lse_g), fin), f"{label}: coverage differs"
+    assert np.all(np.isneginf(lse_g[~fin]))
+    assert np.all(out_g.transpose(0, 2, 1, 3)[~fin] == 0.0), f"{label}: uncovered rows not 0"
+    err = float(np.abs(out_g - out_o).max())
+    lerr = float(np.abs(lse_g[fin] - lse_o[fin]).max()) if fin.any() else 0.0
+    print(f"{label}: out {err:.2e}, lse {lerr:.2e}", flush=True)
+    assert err <= TOL_OUT[dtype] and lerr <= TOL_LSE[dtype], label
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"r{i}" for i in range(N_CASES)])
+def test_random_config(torch_cuda, case):
+    torch = torch_cuda
+    B, N, H, pats, causal, dtype = (case[k] for k in ("B", "N", "H", "patterns", "causal",
+                                                       "dtype"))
+    label = f"{dtype} B{B} N{N} H{H} {pats} causal={causal}"
+    print(label, flush=True)
+    q, k, v = random_inputs(B, N, H, 64, dtype, case["seed"])
+    dout = grad_output(B, N, H, 64, dtype, case["seed"] + 1)
+    qt, kt, vt, dt = (to_torch(x) for x in (q, k, v, dout))
+
+    prob = Problem(qt, kt, vt, pats, causal)
+    prob.out.fill_(float("nan"))
+    prob.lse.fill_(float("nan"))
+    prob.run()
+    bp = BwdProblem(qt, kt, vt, prob.out, prob.lse, dt, pats, causal)
+    for g in (bp.dq, bp.dk, bp.dv):
+        g.fill_(float("nan"))
+    bp.run()
+    torch.cuda.synchronize()
+
+    out_o, lse_o = oracle.fwd(q, k, v, pats, causal=causal)
+    check_fwd(host(prob.out), host(prob.lse), out_o, lse_o, dtype, label)
+
+    grads_o = oracle.bwd(q, k, v, dout, pats, causal=causal)
+    fin = np.isfinite(lse_o).transpose(0, 2, 1)  # [B, N, H]
+    for name, g, o in zip(("dq", "dk", "dv"), (bp.dq, bp.dk, bp.dv), grads_o):
+        g = host(g)
+        assert not np.isnan(g).any(), f"{label}: unwritten {name}"
+        assert np.all(g[~fin] == 0.0), f"{label}: {name} of uncovered rows not 0"
+        scale = max(1.0, float(np.abs(o).max()))
+        err = float(np.abs(g - o).max()) / scale
+        assert err <= TOL_OUT[dtype], f"{label}: {name} error {err}"
+
+    if dtype == "bf16":
+        o1 = torch.full_like(qt, float("nan"))
+        l1 = torch.full_like(prob.lse, float("nan"))
+        try:
+            dilated_attn_onepass(qt, kt, vt, pats, causal, out=o1, lse=l1)
+        except DilatedAttnError as e:
+            assert e.code == -3  # lcm(r) above gcd(w'): no one-pass form
+            return
+        torch.cuda.synchronize()
+        check_fwd(host(o1), host(l1), out_o, lse_o, dtype, label + " one-pass")
