@@ -542,11 +542,11 @@ def main():
         "roofline": roof,
         "detail": {
             "tflops_algorithmic_step": round(step_tflops_alg, 2),
-            "tflops_north_star_formula_step": round(step_tflops_ns, 2),
+            "tflops_nominal_count_step": round(step_tflops_ns, 2),
             "pct_bf16_peak_algorithmic_step": round(100 * step_tflops_alg / peak, 2),
-            "pct_bf16_peak_north_star_formula_step": round(100 * step_tflops_ns / peak, 2),
+            "pct_bf16_peak_nominal_count_step": round(100 * step_tflops_ns / peak, 2),
             "flops_algorithmic": c.flops_alg,
-            "flops_north_star_formula": c.flops_ns,
+            "flops_nominal_count": c.flops_ns,
             "bf16_matmul_8192_tflops": round(matmul_tflops, 1),
             "attn_frac_of_bf16_matmul": round(attn_tflops / matmul_tflops, 4),
             "step_ms_median": round(step_times[K // 2], 4),

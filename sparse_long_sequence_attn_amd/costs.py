@@ -7,7 +7,7 @@ h mod r, L = ceil((w' - off) / r) gathered rows per head and segment):
   (batch, head, segment): S = Q K^T and O = P V, 2 * Dh flops per
   (query, key) pair each. Causal rows see m + 1 keys, so a segment costs
   2 * Dh * L * (L + 1); non-causal 4 * Dh * L^2.
-* spec count: 4 * N * (w / r) * Dh * H per pattern and batch row,
+* nominal count: 4 * N * (w / r) * Dh * H per pattern and batch row,
   halved for causal, with real-valued w / r. It counts every position as a
   query of every pattern, r times the rows a head gathers, so it exceeds the
   algorithmic count by about r for each pattern.
@@ -42,7 +42,7 @@ def lmax(N: int, w: int, r: int) -> int:
 @dataclass
 class Cost:
     flops_alg: float        # useful flops of both contractions
-    flops_ns: float         # spec formula
+    flops_ns: float         # nominal count
     exps: float             # softmax exponentials (one per useful score)
     gathered_rows: int      # sum over patterns, batches, heads, segments of L
     attn_read_bytes: float  # gathered q, k, v rows

@@ -19,7 +19,7 @@ def test_paper_mixture_flops_from_rows_per_head():
     assert c.flops_alg == alg
     assert c.gathered_rows == rows
     assert abs(c.flops_alg / 1e9 - 286.47) < 0.01
-    # spec formula: 4 N (w/r) Dh H per pattern, halved for causal
+    # nominal count: 4 N (w/r) Dh H per pattern, halved for causal
     ns = sum(4 * N * (p["w"] / p["r"]) * Dh * H / 2 for p in g["patterns"])
     assert abs(c.flops_ns - ns) < 1e-3 * ns
 
