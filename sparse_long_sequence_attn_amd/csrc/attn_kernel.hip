@@ -112,9 +112,10 @@ __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // offsets at or past the buffer's range write zeros. Device pass only: the
 // host pass has no such builtin and would drop the kernel's launch stub.
 typedef __attribute__((address_space(3))) char* lds_char_ptr;
-__device__ inline void dma_load16(__amdgpu_buffer_rsrc_t r, lds_char_ptr dst, uint32_t off) {
+__device__ inline void dma_load16(__amdgpu_buffer_rsrc_t r, lds_char_ptr dst, uint32_t off,
+                                  uint32_t soff = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, soff, 0, 0);
 #endif
 }
 
@@ -219,6 +220,10 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   const int32_t qw0 = q0 + wv * QW;
   const int32_t qend_w = min(L, qw0 + QW);
   const int32_t nkt_w = qw0 >= L ? 0 : (CAUSAL ? (qend_w + BN - 1) / BN : nkt);
+  // wave-uniform values the key loop tests, held in scalar registers
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  const int32_t nkt_ws = __builtin_amdgcn_readfirstlane(nkt_w);
+  const int32_t kend_s = __builtin_amdgcn_readfirstlane(CAUSAL ? qw0 + QW : L);
   int32_t mq[QB];  // this lane's queries (gathered indices)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mq[qb] = qw0 + 32 * qb + n;
@@ -352,13 +357,14 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   }
   auto dma_tile = [&](int kt, int buf) {
     if constexpr (DMA) {
+      // the tile's uniform offset goes in the scalar offset field
       const uint32_t base = (uint32_t)kt * tile_bytes;
       const lds_char_ptr kl = (lds_char_ptr)smem + buf * SM::kKElems * 2;
       const lds_char_ptr vl = (lds_char_ptr)smem + (NBUF * SM::kKElems + buf * SM::kVElems) * 2;
 #pragma unroll
       for (int j = 0; j < DW; ++j) {
-        dma_load16(rk, kl + (DW * wv + j) * 1024, base + dk_off[j]);
-        dma_load16(rv, vl + (DW * wv + j) * 1024, base + dv_off[j]);
+        dma_load16(rk, kl + (DW * wvs + j) * 1024, dk_off[j], base);
+        dma_load16(rv, vl + (DW * wvs + j) * 1024, dv_off[j], base);
       }
     }
   };
@@ -447,15 +453,18 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   const float sl2 = a.sl2;
   const int m16 = lane & 15, g16 = lane >> 4;
   bool started = false;  // a tile has set the running max (wave-uniform)
+  int32_t qs_s[QB];      // first query of each of the wave's query blocks
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) qs_s[qb] = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
 
   auto compute = [&](int buf, int kt) {
     const T* K = Ks + buf * SM::kKElems;
     const T* V = Vs + buf * SM::kVElems;
     // key blocks (32 keys) of this tile that some query of the wave sees;
     // later blocks are skipped (their scores stay -inf, their PV is skipped)
-    const int32_t kend = CAUSAL ? qw0 + QW : L;
-    // wave-uniform (kept in a scalar register so the block branches are scalar)
-    const int nkb = __builtin_amdgcn_readfirstlane(min(KB, (kend - kt * BN + 31) / 32));
+    // wave-uniform (scalar registers, so the block branches are scalar);
+    // compute() only runs for tiles that start before kend_s
+    const int nkb = min(KB, (int)((uint32_t)(kend_s - kt * BN + 31) >> 5));
     f32x16 S[KB][QB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -500,7 +509,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
       if (CAUSAL) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const int32_t qs = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
+          const int32_t qs = qs_s[qb];
           if (kb0 == qs) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
@@ -686,7 +695,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
       const int buf = kt & 1;
       // the other buffer was last read before the previous barrier
       if (kt + 1 < nkt) dma_tile(kt + 1, buf ^ 1);
-      if (kt < nkt_w) compute(buf, kt);
+      if (kt < nkt_ws) compute(buf, kt);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's tile writes have landed
       __syncthreads();
     }
