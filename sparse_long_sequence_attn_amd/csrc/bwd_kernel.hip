@@ -332,7 +332,8 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
   const float* lse_row = a.lse + g.bh * a.N;
   const float* d_row = a.dvec + g.bh * a.N;
 
-  // this wave's first key, wave-uniform (scalar branches below)
+  // this wave's index and first key, wave-uniform (scalar branches below)
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
   const int32_t kw0 = __builtin_amdgcn_readfirstlane(k0 + 32 * wv);
   const int32_t mk = kw0 + n;  // this lane's key
   RowFrag<BF> kf, vf;                // B operands of S = Q K^T and dP = dout V^T
@@ -373,8 +374,8 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
     const int32_t m0 = qstart + t * BQ;
     if constexpr (BF) {
       const lds_ptr qt = (lds_ptr)smem + buf * kBufBytes;
-      dmt.load(rq, qt, (uint32_t)m0 * g.mbytes, wv);
-      dmt.load(rdo, qt + kTileBytes, (uint32_t)m0 * g.mbytes, wv);
+      dmt.load(rq, qt, (uint32_t)m0 * g.mbytes, wvs);
+      dmt.load(rdo, qt + kTileBytes, (uint32_t)m0 * g.mbytes, wvs);
     } else {
       stg.load(rq, rdo, (uint32_t)m0 * g.mbytes);
     }
@@ -580,7 +581,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   const auto rv = dev_rsrc(reinterpret_cast<const T*>(a.v) + rowbase, g.range);
   const auto rdo = dev_rsrc(reinterpret_cast<const T*>(a.dout) + rowbase, g.range);
 
-  // this wave's first query, wave-uniform (scalar branches below)
+  // this wave's index and first query, wave-uniform (scalar branches below)
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
   const int32_t qw0 = __builtin_amdgcn_readfirstlane(q0 + 32 * wv);
   const int32_t mq = qw0 + n;  // this lane's query
   RowFrag<BF> qf, df;                // B operands of S^T = K Q^T and dP^T = V dout^T
@@ -603,7 +605,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   const int32_t qend_wg = min(g.L, q0 + 32 * NW);
   const int32_t nkt = CAUSAL ? (qend_wg + BK - 1) / BK : (g.L + BK - 1) / BK;
   const int32_t qend_w = min(g.L, qw0 + 32);
-  const int32_t nkt_w = qw0 >= g.L ? 0 : (CAUSAL ? (qend_w + BK - 1) / BK : nkt);
+  const int32_t nkt_w =
+      __builtin_amdgcn_readfirstlane(qw0 >= g.L ? 0 : (CAUSAL ? (qend_w + BK - 1) / BK : nkt));
 
   PairStager<BF, BF ? NT / 8 : BK, NT> stg;  // fp32 only
   DmaTile<BK, NW> dmt;                      // bf16 only
@@ -615,8 +618,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   auto load_tile = [&](int t, int buf) {
     if constexpr (BF) {
       const lds_ptr kt = (lds_ptr)smem + buf * kBufBytes;
-      dmt.load(rk, kt, (uint32_t)(t * BK) * g.mbytes, wv);
-      dmt.load(rv, kt + kTileBytes, (uint32_t)(t * BK) * g.mbytes, wv);
+      dmt.load(rk, kt, (uint32_t)(t * BK) * g.mbytes, wvs);
+      dmt.load(rv, kt + kTileBytes, (uint32_t)(t * BK) * g.mbytes, wvs);
     } else {
       stg.load(rk, rv, (uint32_t)(t * BK) * g.mbytes);
     }

@@ -43,9 +43,10 @@ __device__ inline u32x2 dev_read_tr16(lds_cptr base, uint32_t byte_off) {
 // offsets at or past the buffer's range. Device pass only: the host pass
 // has no such builtin and would drop the kernel's launch stub.
 typedef __attribute__((address_space(3))) char* lds_ptr;
-__device__ inline void dev_dma16(__amdgpu_buffer_rsrc_t r, lds_ptr dst, uint32_t off) {
+__device__ inline void dev_dma16(__amdgpu_buffer_rsrc_t r, lds_ptr dst, uint32_t off,
+                                 uint32_t soff = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, soff, 0, 0);
 #endif
 }
 
@@ -62,7 +63,9 @@ __device__ inline int dma_slot(int R, int c) {
 
 // Stages BR rows of one tensor with NW waves: each wave issues DW loads of
 // 1 KiB (8 rows); lane i of load j fetches the chunk that belongs at its
-// slot.
+// slot. load() takes the wave index and the tile's byte offset as
+// wave-uniform values (scalar registers: the offset goes in the loads'
+// scalar offset field).
 template <int BR, int NW>
 struct DmaTile {
   static constexpr int DW = BR * 128 / 1024 / NW;
@@ -78,7 +81,7 @@ struct DmaTile {
   __device__ inline void load(__amdgpu_buffer_rsrc_t r, lds_ptr tile, uint32_t base,
                               int wv) const {
 #pragma unroll
-    for (int j = 0; j < DW; ++j) dev_dma16(r, tile + (DW * wv + j) * 1024, base + off[j]);
+    for (int j = 0; j < DW; ++j) dev_dma16(r, tile + (DW * wv + j) * 1024, off[j], base);
   }
 };
 
