@@ -691,13 +691,19 @@ __global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const At
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if constexpr (DMA) {
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int buf = kt & 1;
+    // unrolled by two so each step's buffer is a compile-time constant: the
+    // LDS reads then carry the buffer offset as an immediate
+    auto step = [&](auto bufc, int kt) {
+      constexpr int buf = decltype(bufc)::value;
       // the other buffer was last read before the previous barrier
       if (kt + 1 < nkt) dma_tile(kt + 1, buf ^ 1);
       if (kt < nkt_ws) compute(buf, kt);
       __builtin_amdgcn_s_waitcnt(0);  // this wave's tile writes have landed
       __syncthreads();
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nkt) step(std::integral_constant<int, 1>{}, kt + 1);
     }
   } else if constexpr (NBUF == 2) {
     for (int kt = 0; kt < nkt; ++kt) {
