@@ -522,14 +522,23 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
   store_tile(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < nqt; ++t) {
-    const int buf = t & 1;
+  // bf16: unrolled by two so each step's buffer is a compile-time constant
+  auto step = [&](auto bufc, int t) {
+    const int buf = bufc;
     // the other buffer was last read before the previous barrier
     if (t + 1 < nqt) load_tile(t + 1, buf ^ 1);
     compute(buf, t);
     if (t + 1 < nqt) store_tile(buf ^ 1);
     if constexpr (BF) __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
     __syncthreads();
+  };
+  if constexpr (BF) {
+    for (int t = 0; t < nqt; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nqt) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  } else {  // the fp32 tiles keep the rolled loop: unrolled, they spill
+    for (int t = 0; t < nqt; ++t) step(t & 1, t);
   }
 
   const PatDev& P = a.pat[tl.p];
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
 // ---------------------------------------------------------------- dQ
 
 template <int NW, bool CAUSAL, bool BF>
-__global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
+__global__ __launch_bounds__(NW * 64, BF ? 4 : 1) void bwd_q_kernel(const BwdArgs a) {
   static_assert(NW == 4, "segments of at most 32 rows take bwd_short_kernel");
   using T = typename std::conditional<BF, __bf16, float>::type;
   constexpr int BK = 64;  // key rows per LDS tile
@@ -717,14 +726,24 @@ __global__ __launch_bounds__(NW * 64) void bwd_q_kernel(const BwdArgs a) {
   store_tile(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
+  // bf16: unrolled by two so each step's buffer is a compile-time constant
+  // (LDS reads then carry the buffer offset as an immediate)
+  auto step = [&](auto bufc, int t) {
+    const int buf = bufc;
     // the other buffer was last read before the previous barrier
     if (t + 1 < nkt) load_tile(t + 1, buf ^ 1);
     if (t < nkt_w) compute(buf, t);
     if (t + 1 < nkt) store_tile(buf ^ 1);
     if constexpr (BF) __builtin_amdgcn_s_waitcnt(0);  // this wave's tile loads have landed
     __syncthreads();
+  };
+  if constexpr (BF) {
+    for (int t = 0; t < nkt; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nkt) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  } else {  // the fp32 tiles keep the rolled loop: unrolled, they spill
+    for (int t = 0; t < nkt; ++t) step(t & 1, t);
   }
 
   const PatDev& P = a.pat[tl.p];
