@@ -38,13 +38,15 @@ __device__ inline uint32_t pack_bf16(float x, float y) {
 }
 
 template <bool BF, int NP>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a, const FastDiv h_div) {
-  // blockIdx.y = batch; rows of one batch are (t, h) pairs in output order
+__global__ __launch_bounds__(kThreads) void merge_kernel(const MergeArgs a, const FastDiv n_div) {
+  // blockIdx.y = batch; rows of one batch are taken head by head (h, t), so
+  // a block's rows are consecutive positions of one head: each pattern's
+  // partial rows and the lse values are then contiguous runs
   const uint32_t row = blockIdx.x * kRowsPerBlock + (threadIdx.x / kLanesPerRow);
   const int sub = threadIdx.x % kLanesPerRow;
   if (row >= (uint32_t)(a.N * a.H)) return;
-  const uint32_t t = fdiv(row, h_div);
-  const int32_t h = (int32_t)(row - t * (uint32_t)a.H);
+  const int32_t h = (int32_t)fdiv(row, n_div);
+  const uint32_t t = row - (uint32_t)h * (uint32_t)a.N;
   const int64_t b = blockIdx.y;
 
   // rows exactly one pattern gathers were written by the attention kernel
@@ -142,7 +144,7 @@ hipError_t launch_merge_np(const MergeArgs& a, dim3 g, dim3 b, const FastDiv& hd
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t st) {
   const int64_t rows = a.N * a.H;
   dim3 g((uint32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock), (uint32_t)a.B), b(kThreads);
-  const FastDiv hd = make_fastdiv((uint32_t)a.H);
+  const FastDiv hd = make_fastdiv((uint32_t)a.N);
   return bf16 ? launch_merge_np<true>(a, g, b, hd, st) : launch_merge_np<false>(a, g, b, hd, st);
 }
 
