@@ -150,9 +150,10 @@ int dilated_attn_fwd_merge(const void* q, const void* k, const void* v, void* ou
  * contents on entry are ignored. */
 
 /* Bytes of device workspace dilated_attn_bwd needs: one float per row for D
- * and, for two or more patterns, the per-pattern fp32 partial dq, dk, dv rows
- * of rows several patterns gather. Writes *bytes and returns DA_OK, or an
- * error code for invalid arguments. */
+ * and, for two or more patterns, the per-pattern partial dq, dk, dv rows of
+ * rows several patterns gather, in the gradients' dtype (so the size depends
+ * on dtype). Writes *bytes and returns DA_OK, or an error code for invalid
+ * arguments. */
 int dilated_attn_bwd_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
                                      const da_pattern* patterns, int32_t n_patterns,
                                      int32_t dtype, size_t* bytes);

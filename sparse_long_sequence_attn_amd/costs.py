@@ -126,8 +126,9 @@ def bwd_cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causa
     Each gathered row of each pattern is read once by each of the two main
     kernels (q, k, v, dout rows plus its lse and D); rows one pattern
     gathers are written once as final gradients, rows several patterns
-    gather once per covering pattern as fp32 partials (Dh floats per
-    gradient), which the merge kernel reads back before writing the sums
+    gather once per covering pattern as partials in the gradients' dtype
+    (Dh elements per gradient), which the merge kernel reads back before
+    writing the sums
     and the zero rows of positions no pattern gathers. When every segment
     gathers at most 32 rows one kernel reads each gathered row's q, k, v,
     dout, out and lse once and writes its three gradients (D is formed on
@@ -136,7 +137,7 @@ def bwd_cost(B: int, N: int, H: int, Dh: int, patterns: Sequence[Pattern], causa
     pairs = fwd.flops_alg / (4.0 * Dh)
     rows = fwd.gathered_rows
     row = Dh * elem_bytes
-    prow = Dh * 4.0
+    prow = Dh * elem_bytes  # partial rows have the gradients' dtype
     t = np.arange(N, dtype=np.int64)
     single = multi_slots = multi_rows = none = 0
     for h in range(H):

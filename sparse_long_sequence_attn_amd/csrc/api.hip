@@ -161,13 +161,15 @@ int make_plan(int64_t B, int64_t N, int32_t H, int32_t Dh, const da_pattern* pat
   }
   pl->ws_bytes = (size_t)cur * 4;
 
-  // backward: D per row, then dq, dk, dv partial blocks per pattern
+  // backward: D per row, then dq, dk, dv partial blocks per pattern, in the
+  // gradients' dtype (offsets and sizes here count 4-byte words)
   cur = align64(B * H * N);
   for (int i = 0; i < n_patterns; ++i) {
     pl->bwd_po_off[i] = -1;
     if (n_patterns > 1) {
       pl->bwd_po_off[i] = cur;
-      cur += align64(3 * B * H * pl->pat[i].nseg * pl->pat[i].lmax * kDh);
+      const int64_t elems = 3 * B * H * pl->pat[i].nseg * pl->pat[i].lmax * kDh;
+      cur += align64(pl->bf16 ? elems / 2 : elems);  // kDh is even
     }
   }
   pl->bwd_ws_bytes = (size_t)cur * 4;

@@ -29,8 +29,9 @@
 //  * bwd_q_kernel: one workgroup per tile of 128 gathered queries, in the
 //    forward kernel's layout (S^T = K Q^T: one query per lane), K and V
 //    streamed through LDS; dQ^T += K^T dS^T takes K^T from the transpose read.
-//  * bwd_merge_kernel: rows several patterns gather add up their fp32
-//    partials; rows no pattern gathers get zero gradients.
+//  * bwd_merge_kernel: rows several patterns gather add up their partials
+//    (stored in the gradients' dtype, summed in fp32); rows no pattern
+//    gathers get zero gradients.
 // bf16 inputs use v_mfma_f32_32x32x16_bf16 with P and dS rounded to bf16 as
 // MFMA operands; fp32 inputs use v_mfma_f32_32x32x2_f32 throughout.
 //
@@ -207,7 +208,8 @@ struct PairStager {
 
 // Writes one lane's half of a gradient row held in MFMA output layout (two
 // 32-dim blocks; register 4g + e of block db is dim db*32 + 8g + 4hh + e),
-// multiplied by mul, either into the final tensor or into an fp32 partial.
+// multiplied by mul, either into the final tensor or into a partial row
+// (the partials have the gradients' dtype: 64 contiguous elements per row).
 template <bool BF>
 __device__ inline void put_row(void* dst_tensor, int64_t elem_off, const f32x16 (&acc)[2],
                                float mul, int hh) {
@@ -228,19 +230,6 @@ __device__ inline void put_row(void* dst_tensor, int64_t elem_off, const f32x16 
         for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * mul;
         *reinterpret_cast<f32x4*>(dst + d) = x;
       }
-    }
-}
-
-__device__ inline void put_partial(float* dst, const f32x16 (&acc)[2], float mul, int hh) {
-  dst += 4 * hh;
-#pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = acc[db][4 * g + e] * mul;
-      *reinterpret_cast<f32x4*>(dst + db * 32 + 8 * g) = x;
     }
 }
 
@@ -265,10 +254,12 @@ __device__ inline void stage_row(float* srow, const f32x16 (&acc)[2], float mul,
 }
 
 // Rows of kind 1 go to final + pos * rs, rows of kind 2 to partial + R * kDh
-// (the wave's first gathered row at partial); kind 0 rows are skipped.
+// (the wave's first gathered row at partial, in the gradients' dtype); kind 0
+// rows are skipped.
 template <bool BF>
-__device__ inline void write_rows(const float* srow, const int32_t* mpos, const int32_t* mkind,
-                                  void* final_base, int64_t rs, float* partial, int lane) {
+__device__ inline void write_rows(
+    const float* srow, const int32_t* mpos, const int32_t* mkind, void* final_base, int64_t rs,
+    typename std::conditional<BF, __bf16, float>::type* partial, int lane) {
   using T = typename std::conditional<BF, __bf16, float>::type;
   const int sr = lane >> 4, sc = lane & 15;
 #pragma unroll
@@ -277,15 +268,12 @@ __device__ inline void write_rows(const float* srow, const int32_t* mpos, const 
     const int32_t kind = mkind[R];
     if (kind == 0) continue;
     const f32x4 x = *reinterpret_cast<const f32x4*>(srow + R * kStageStride + 4 * sc);
-    if (kind == 1) {
-      T* dst = reinterpret_cast<T*>(final_base) + (int64_t)mpos[R] * rs + 4 * sc;
-      if constexpr (BF)
-        *reinterpret_cast<u32x2*>(dst) = u32x2{dev_pack_bf16(x[0], x[1]), dev_pack_bf16(x[2], x[3])};
-      else
-        *reinterpret_cast<f32x4*>(dst) = x;
-    } else {
-      *reinterpret_cast<f32x4*>(partial + (int64_t)R * kDh + 4 * sc) = x;
-    }
+    T* dst = kind == 1 ? reinterpret_cast<T*>(final_base) + (int64_t)mpos[R] * rs + 4 * sc
+                       : partial + (int64_t)R * kDh + 4 * sc;
+    if constexpr (BF)
+      *reinterpret_cast<u32x2*>(dst) = u32x2{dev_pack_bf16(x[0], x[1]), dev_pack_bf16(x[2], x[3])};
+    else
+      *reinterpret_cast<f32x4*>(dst) = x;
   }
 }
 
@@ -551,8 +539,8 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
     put_row<BF>(a.dk, e, dK, a.scale, hh);
     put_row<BF>(a.dv, e, dV, 1.f, hh);
   } else {
-    put_partial(a.ws + P.po_off + (slots + prow0 + mk) * kDh, dK, a.scale, hh);
-    put_partial(a.ws + P.po_off + (2 * slots + prow0 + mk) * kDh, dV, 1.f, hh);
+    put_row<BF>(a.ws + P.po_off, (slots + prow0 + mk) * kDh, dK, a.scale, hh);
+    put_row<BF>(a.ws + P.po_off, (2 * slots + prow0 + mk) * kDh, dV, 1.f, hh);
   }
 }
 
@@ -752,7 +740,7 @@ __global__ __launch_bounds__(NW * 64, BF ? 4 : 1) void bwd_q_kernel(const BwdArg
   if (coverage(a, (uint32_t)pos, tl.h) == 1) {
     put_row<BF>(a.dq, g.headbase + pos * g.rs, dQ, a.scale, hh);
   } else {
-    put_partial(a.ws + P.po_off + (prow0 + mq) * kDh, dQ, a.scale, hh);
+    put_row<BF>(a.ws + P.po_off, (prow0 + mq) * kDh, dQ, a.scale, hh);
   }
 }
 
@@ -1159,7 +1147,7 @@ __global__ __launch_bounds__(64, (QKN && BF) ? 3 : 1) void bwd_short_kernel(cons
     mpos[n] = n < g.L ? (int32_t)pos : -1;  // positions are below 2^31
     mkind[n] = kind;
   }
-  float* const part = a.ws + P.po_off + prow0 * kDh;
+  T* const part = reinterpret_cast<T*>(a.ws + P.po_off) + prow0 * kDh;
   stage_row(srow, dQ, a.scale, n, hh);
   XRow<BF> xk[QKN ? 8 : 1];  // QKN: k's input rows for the dk epilogue
   if constexpr (QKN) load_rows_x<BF>(xk, rk, mbytes_in, lane);
@@ -1262,10 +1250,10 @@ __global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(const BwdRowArgs 
 
 // Sum of the per-pattern partials of rows two or more patterns gather; zero
 // gradients for rows no pattern gathers. Rows one pattern gathers were
-// written by the dK/dV and dQ kernels (or the short-segment kernel). For
-// each gradient in turn, every covering pattern's partial is loaded before
-// any is added, so a row costs three memory round trips rather than one per
-// pattern and gradient; instantiated per pattern count.
+// written by the dK/dV and dQ kernels (or the short-segment kernel). Every
+// covering pattern's partials of all three gradients are loaded before any
+// is added, so a row costs one memory round trip rather than one per pattern
+// and gradient; instantiated per pattern count.
 template <bool BF, int NP>
 __global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs a,
                                                                const FastDiv h_div) {
@@ -1287,30 +1275,51 @@ __global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs
 
   const int64_t elem = (b * a.N + t) * a.grad_rs + (int64_t)h * kDh + kDimsPerLane * sub;
   void* const dst[3] = {a.dq, a.dk, a.dv};
+  // every covering pattern's partials of all three gradients are loaded
+  // before any is added (the sum is taken in fp32)
+  using Raw = typename std::conditional<BF, u32x4[2], f32x4[4]>::type;
+  Raw x[3][NP];
 #pragma unroll
-  for (int w = 0; w < 3; ++w) {
-    f32x4 x[NP][4];
+  for (int w = 0; w < 3; ++w)
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (ci[i] < 0) continue;
       const PatDev& P = a.pat[i];
       const int64_t slots = P.units * P.lmax;
       const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.ws + P.po_off + (w * slots + prow) * kDh +
-                                                        kDimsPerLane * sub);
+      const int64_t e = (w * slots + prow) * kDh + kDimsPerLane * sub;
+      if constexpr (BF) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.ws + P.po_off) + e);
+        x[w][i][0] = p[0];
+        x[w][i][1] = p[1];
+      } else {
+        const f32x4* p = reinterpret_cast<const f32x4*>(a.ws + P.po_off + e);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) x[i][j] = src[j];
+        for (int j = 0; j < 4; ++j) x[w][i][j] = p[j];
+      }
     }
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
     float acc[kDimsPerLane];
 #pragma unroll
     for (int e = 0; e < kDimsPerLane; ++e) acc[e] = 0.f;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (ci[i] < 0) continue;
+      if constexpr (BF) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * j + e] += x[i][j][e];
+          for (int k = 0; k < 4; ++k) {
+            acc[8 * j + 2 * k] += __uint_as_float(x[w][i][j][k] << 16);
+            acc[8 * j + 2 * k + 1] += __uint_as_float(x[w][i][j][k] & 0xffff0000u);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[4 * j + k] += x[w][i][j][k];
+      }
     }
     store16<BF>(dst[w], elem, acc);
   }

@@ -198,17 +198,17 @@ def test_bwd_empty_problems_are_accepted_without_launch(lib):
                    dq=None, dk=None, dv=None, ws=None, wsb=0) == 0
 
 
-def bwd_ws_expected(B, N, H, pats):
+def bwd_ws_expected(B, N, H, pats, es):
     """Backward workspace from the documented layout: a float D per row
-    (rounded up to 256 bytes), then for two or more patterns three float
-    partial rows (dq, dk, dv) per gathered row slot, per pattern rounded up
-    to 256 bytes."""
+    (rounded up to 256 bytes), then for two or more patterns three partial
+    rows (dq, dk, dv) per gathered row slot in the gradients' dtype (es bytes
+    an element), per pattern rounded up to 256 bytes."""
     tot = -(-B * H * N * 4 // 256) * 256
     if len(pats) > 1:
         for (w, r) in pats:
             wp = min(w, N)
             rows = B * H * (N // wp) * (-(-wp // r))
-            tot += -(-3 * rows * 64 * 4 // 256) * 256
+            tot += -(-3 * rows * 64 * es // 256) * 256
     return tot
 
 
@@ -218,9 +218,10 @@ def bwd_ws_expected(B, N, H, pats):
     (1, 32768, 16, [(2048, 1), (4096, 2), (8192, 4), (16384, 6), (32768, 12)]),
     (2, 96, 3, [(1000, 7), (8, 1), (96, 96)]),
 ])
-def test_bwd_workspace_bytes(B, N, H, pats):
-    got = _native.bwd_workspace_bytes(B, N, H, 64, pats, _native.DA_BF16)
-    assert got == bwd_ws_expected(B, N, H, pats)
+@pytest.mark.parametrize("dtype,es", [(_native.DA_BF16, 2), (_native.DA_F32, 4)])
+def test_bwd_workspace_bytes(B, N, H, pats, dtype, es):
+    got = _native.bwd_workspace_bytes(B, N, H, 64, pats, dtype)
+    assert got == bwd_ws_expected(B, N, H, pats, es)
 
 
 def test_bwd_workspace_bytes_errors(lib):
