@@ -1289,7 +1289,8 @@ __global__ __launch_bounds__(kRowThreads) void bwd_merge_kernel(const BwdRowArgs
       const int64_t prow = (b * a.H + h) * P.nseg * P.lmax + ci[i];
       const int64_t e = (w * slots + prow) * kDh + kDimsPerLane * sub;
       if constexpr (BF) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.ws + P.po_off) + e);
+        const u32x4* p =
+            reinterpret_cast<const u32x4*>(reinterpret_cast<const __bf16*>(a.ws + P.po_off) + e);
         x[w][i][0] = p[0];
         x[w][i][1] = p[1];
       } else {
