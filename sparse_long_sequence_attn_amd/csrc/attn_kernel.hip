@@ -161,7 +161,9 @@ struct Smem {
 // loaded (one-wave workgroups only): each 64-value row becomes
 // (x - mean) / sqrt(var + eps) * gain + bias, statistics in fp32.
 template <int NW, int QB, int BN, bool CAUSAL, bool FINAL, bool BF, bool QKN = false>
-__global__ __launch_bounds__(NW * 64, QKN ? 3 : 4) void attn_fwd_kernel(const AttnArgs a) {
+// (fp32 with qk_norm: 2 waves per SIMD, which its registers need without spills)
+__global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kernel(
+    const AttnArgs a) {
   static_assert(!QKN || (NW == 1 && QB == 1), "qk_norm is fused into one-wave workgroups only");
   using T = typename std::conditional<BF, __bf16, float>::type;
   // one-wave workgroups serve segments of at most 32 gathered rows (one key
@@ -919,7 +921,9 @@ struct OnePat {
 // layouts of attn_fwd_kernel's 4-wave path); the key tiles of all covering
 // patterns go through one online softmax, and every row is written final.
 template <bool CAUSAL>
-__global__ __launch_bounds__(64 * kOnePassWaves, 4) void attn_onepass_kernel(const OnePassArgs a) {
+// (non-causal: 3 waves per SIMD, which its registers need without spills)
+__global__ __launch_bounds__(64 * kOnePassWaves, CAUSAL ? 4 : 3) void attn_onepass_kernel(
+    const OnePassArgs a) {
   constexpr int NW = kOnePassWaves, BN = 64, KB = BN / 32, BM = 32 * NW;
   constexpr int DW = BN * 128 / 1024 / NW;
   using T = __bf16;
