@@ -2,7 +2,7 @@
 import json
 import os
 
-from sparse_long_sequence_attn_amd.costs import cost
+from sparse_long_sequence_attn_amd.costs import bwd_cost, cost
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -47,3 +47,33 @@ def test_merge_traffic_split():
     assert c.attn_write_bytes == 8 * out_row + 16 * part_row
     assert c.merge_read_bytes == 16 * part_row
     assert c.merge_write_bytes == 8 * out_row
+
+
+
+def test_bwd_partial_traffic_split():
+    # patterns (64, 1) and (128, 2) at N = 128, one head (offset 0): the 64
+    # even positions are gathered by both patterns (128 partial slots per
+    # gradient), the 64 odd ones by the first only (final rows). Partial rows
+    # have the gradients' dtype (es bytes an element); the merge reads them
+    # and writes the 64 summed rows of each of the 3 gradients.
+    for es in (2, 4):
+        c = bwd_cost(1, 128, 1, 64, [(64, 1), (128, 2)], True, es)
+        assert not c.fused
+        row = 64 * es
+        assert c.merge_bytes == 3 * 128 * row + 3 * 64 * row
+        reads = (128 + 64) * (4 * row + 8)  # q, k, v, dout rows + lse, D
+        assert c.kv_bytes == reads + 2 * (64 * row + 128 * row)
+        assert c.q_bytes == reads + (64 * row + 128 * row)
+        assert c.prep_bytes == 128 * (2 * row + 4)
+
+
+def test_bwd_fused_short_segments_traffic():
+    # segments of at most 32 gathered rows: one kernel reads q, k, v, dout,
+    # out rows + lse once and writes final rows or partials (same split as
+    # above at N = 16 with patterns (4, 1) and (8, 2))
+    for es in (2, 4):
+        c = bwd_cost(1, 16, 1, 64, [(4, 1), (8, 2)], True, es)
+        assert c.fused
+        row = 64 * es
+        assert c.kv_bytes == (16 + 8) * (5 * row + 4) + 3 * 8 * row + 3 * 16 * row
+        assert c.merge_bytes == 3 * 16 * row + 3 * 8 * row
