@@ -65,6 +65,18 @@ def measured_traffic(which, workload):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, heads):
     """The oracle (as it stands) on the first `heads` heads of the workload:
     heads are independent, so the full workload costs H / heads times as much."""
@@ -83,9 +95,65 @@ def cpu_baseline(w, heads):
         "value": w.tokens / full,
         "unit": "tokens/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"heads 0-{heads - 1} of {w.H} of the same workload (all {w.B * w.N} tokens, "
                   f"all patterns), fp64 C oracle, {dt:.2f} s measured, scaled by {w.H}/{heads}",
+    }
+
+
+def oracle_row_sample(w, per_head):
+    """A deterministic row sample of a workload too large for the whole
+    oracle: for every head, the first and last gathered position of every
+    segment of every pattern, then evenly spaced positions up to `per_head`
+    rows. Returns int64 [n, 3] of (b, t, h), batch 0."""
+    import numpy as np
+
+    rows = []
+    for h in range(w.H):
+        ts = set()
+        for (pw, r) in w.patterns:
+            wp = min(pw, w.N)
+            off = h % r
+            last = off + ((wp - 1 - off) // r) * r
+            starts = np.arange(0, w.N, wp)
+            ts.update((starts + off).tolist())
+            ts.update((starts + last).tolist())
+        fill = per_head - len(ts)
+        if fill > 0:
+            for t in np.linspace(0, w.N - 1, fill + len(ts)).astype(np.int64).tolist():
+                if len(ts) >= per_head:
+                    break
+                ts.add(int(t))
+        rows.extend((0, t, h) for t in sorted(ts))
+    return np.array(rows, dtype=np.int64)
+
+
+def cpu_baseline_sampled(w, q, k, v, per_head):
+    """The row-wise oracle (as it stands) on a deterministic row sample of a
+    device-generated workload, with the time extrapolated linearly to all
+    B * N * H rows."""
+    import oracle
+    from sparse_long_sequence_attn_amd.workloads import from_torch_bits
+
+    qh, kh, vh = (from_torch_bits(x) for x in (q, k, v))
+    rows = oracle_row_sample(w, per_head)
+    t0 = time.perf_counter()
+    oracle.rows(qh, kh, vh, w.patterns, rows, causal=w.causal)
+    dt = time.perf_counter() - t0
+    total = w.B * w.N * w.H
+    full = dt * total / len(rows)
+    return {
+        "value": w.tokens / full,
+        "unit": "tokens/s",
+        "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
+        "kind": "oracle",
+        "sample": f"{len(rows)} rows (every head: each pattern's first and last gathered row "
+                  f"of every segment, then evenly spaced positions; {per_head} rows per head) "
+                  f"of the same workload, fp64 C row-wise oracle, {dt:.2f} s measured; value is "
+                  f"a LINEAR EXTRAPOLATION by row count to all {total} rows "
+                  f"({full:.0f} s estimated)",
     }
 
 
@@ -107,6 +175,7 @@ def cpu_baseline_bwd(w, heads):
         "value": w.tokens / full,
         "unit": "tokens/s",
         "cores": oracle.max_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"backward, heads 0-{heads - 1} of {w.H} of the same workload (all "
                   f"{w.B * w.N} tokens, all patterns), fp64 C oracle, {dt:.2f} s measured, "
@@ -384,6 +453,9 @@ def main():
     ap.add_argument("--workload", default="paper_mixture_n32768_h16_bf16")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=8192,
+                    help="rows per head of the CPU oracle's sample on device-generated "
+                         "workloads (the million-token one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "module"], default="fwd")
     ap.add_argument("--gemm-tuning", choices=["on", "off"], default="on",
@@ -568,7 +640,10 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H))
+        if w.device_generated:
+            result["cpu_baseline"] = cpu_baseline_sampled(w, q, k, v, args.cpu_rows_per_head)
+        else:
+            result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H))
     print(json.dumps(result), flush=True)
 
 

@@ -65,12 +65,11 @@ class Problem:
             (self.B, self.H, self.N), dtype=torch.float32, device=q.device)
         if workspace is None:
             workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        _check_workspace(workspace, q.device)
         self.workspace = workspace
         self.ws_bytes = workspace.numel() * workspace.element_size()
-        if self.out.shape != q.shape or self.out.dtype != q.dtype or not self.out.is_contiguous():
-            raise ValueError("out must be a contiguous tensor like q")
-        if self.lse.shape != (self.B, self.H, self.N) or self.lse.dtype != torch.float32:
-            raise ValueError("lse must be float32 [B, H, N]")
+        _check_out("out", self.out, q.shape, q.dtype, q.device)
+        _check_out("lse", self.lse, (self.B, self.H, self.N), torch.float32, q.device)
 
     def _call(self, fn_name, stream=None):
         import torch
@@ -129,11 +128,11 @@ class BwdProblem:
         self.dk = dk if dk is not None else torch.empty_like(q)
         self.dv = dv if dv is not None else torch.empty_like(q)
         for name, t in (("dq", self.dq), ("dk", self.dk), ("dv", self.dv)):
-            if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-                raise ValueError(f"{name} must be a contiguous tensor like q")
+            _check_out(name, t, q.shape, q.dtype, q.device)
         ws = bwd_workspace_bytes(self.B, self.N, self.H, self.Dh, self.patterns, self.dtype)
         if workspace is None:
             workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+        _check_workspace(workspace, q.device)
         self.workspace = workspace
         self.ws_bytes = workspace.numel() * workspace.element_size()
 
@@ -245,6 +244,8 @@ def qk_norm_fwd(xq, xk, gain_q, bias_q, gain_k, bias_k, eps=1e-5, yq=None, yk=No
         raise ValueError("xq and xk must share a shape ending in 64")
     yq = torch.empty_like(xq) if yq is None else yq
     yk = torch.empty_like(xk) if yk is None else yk
+    _check_out("yq", yq, xq.shape, xq.dtype, xq.device)
+    _check_out("yk", yk, xk.shape, xk.dtype, xk.device)
     rows = xq.numel() // DA_HEAD_DIM
     code = load_library().dilated_attn_qk_norm_fwd(
         xq.data_ptr(), xk.data_ptr(), gain_q.data_ptr(), bias_q.data_ptr(), gain_k.data_ptr(),
@@ -297,6 +298,15 @@ def _check_out(name, t, shape, dtype, device):
             or t.device != device or not t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
                          f"on {device}")
+
+
+def _check_workspace(t, device):
+    """The library cannot tell host from device memory: a workspace must be
+    a contiguous tensor on the inputs' GPU."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
 
 
 def _row_stride(named):
@@ -383,6 +393,7 @@ def dilated_attn_qknorm_bwd(xq, xk, v, gain_q, bias_q, gain_k, bias_k, out, lse,
     if workspace is None:
         ws = _native.bwd_qknorm_workspace_bytes(B, N, H, Dh, pats, dt)
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=xq.device)
+    _check_workspace(workspace, xq.device)
     if dxq is None and dxk is None and dv is None:
         if rs == 0:
             dxq, dxk, dv = (torch.empty((B, N, H, Dh), dtype=xq.dtype, device=xq.device)

@@ -229,6 +229,43 @@ def test_empty_inputs_and_errors(torch_cuda):
         dilated_attn(x.cpu(), x.cpu(), x.cpu(), [(16, 2)])
 
 
+def test_caller_buffers_checked_before_launch(torch_cuda):
+    """The C ABI cannot tell host memory from device memory, so the binding
+    rejects caller-given outputs and workspaces that are on the host, on
+    another device or strided, with ValueError and before any launch."""
+    torch = torch_cuda
+    from sparse_long_sequence_attn_amd import BwdProblem, dilated_attn_bwd, qk_norm_fwd
+
+    x = torch.zeros((1, 64, 4, 64), dtype=torch.bfloat16, device="cuda")
+    pats = [(16, 2), (64, 1)]
+    good_out = torch.empty_like(x)
+    good_lse = torch.empty((1, 4, 64), dtype=torch.float32, device="cuda")
+    bad = {
+        "out": [good_out.cpu(), torch.empty((1, 64, 64, 4), dtype=torch.bfloat16,
+                                            device="cuda").transpose(2, 3)],
+        "lse": [good_lse.cpu(), torch.empty((1, 64, 4), dtype=torch.float32,
+                                            device="cuda").transpose(1, 2)],
+        "workspace": [torch.empty(1 << 20, dtype=torch.uint8),
+                      torch.empty(2 << 20, dtype=torch.uint8, device="cuda")[::2]],
+    }
+    for name, cases in bad.items():
+        for t in cases:
+            with pytest.raises(ValueError, match=name):
+                dilated_attn(x, x, x, pats, **{name: t})
+    fp = Problem(x, x, x, pats)
+    fp.run()
+    for name in ("dq", "dk", "dv"):
+        with pytest.raises(ValueError, match=name):
+            dilated_attn_bwd(x, x, x, fp.out, fp.lse, x, pats, **{name: good_out.cpu()})
+    with pytest.raises(ValueError, match="workspace"):
+        BwdProblem(x, x, x, fp.out, fp.lse, x, pats, workspace=torch.empty(1 << 20,
+                                                                           dtype=torch.uint8))
+    g = torch.ones(64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="yq"):
+        qk_norm_fwd(x, x, g, g, g, g, yq=good_out.cpu())
+    torch.cuda.synchronize()
+
+
 def test_single_pattern_equals_full_attention_sdpa(torch_cuda):
     """w = N, r = 1 against torch's own attention on the GPU in fp32 (an
     independent check of the kernel besides the oracle)."""
