@@ -291,6 +291,28 @@ int dilated_attn_fwd_onepass(const void* q, const void* k, const void* v, void* 
                              const da_pattern* patterns, int32_t n_patterns, int32_t causal,
                              int32_t dtype, float scale, void* stream);
 
+/* ------------------------------------------------------------------ no allocation
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the whole
+ * forward pass of dilated_attn_fwd with the workspace taken from a
+ * file-scope device array of DA_NOALLOC_MAX_WORKSPACE_BYTES bytes inside
+ * the library instead of a caller buffer. The array exists once per GPU the
+ * library runs on and is held until the process ends; its address is looked
+ * up once per device (hipGetSymbolAddress). The call allocates nothing.
+ * Problems whose dilated_attn_workspace_bytes() exceeds the array return
+ * DA_ERR_WORKSPACE before anything is launched; DA_ERR_LAUNCH also covers a
+ * failed address lookup. All calls on one GPU share that GPU's array and
+ * nothing in it needs clearing between calls, but calls that overlap in
+ * time on one GPU (different streams, or host threads) race on it: the
+ * caller must order them. Arguments, other checks and outputs as
+ * dilated_attn_fwd without the workspace; results are bit-identical to it. */
+#define DA_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)64 << 20)
+int dilated_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t N, int32_t H, int32_t Dh,
+                             const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                             int32_t dtype, float scale, void* stream);
+
 /* Test hook: the gather map the kernels use, written by a device kernel
  * through the same index function as the attention kernel.
  * dev_out: device int64 [N / min(w, N)][ceil(min(w, N) / r)], segment-major;

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(PKG, "libdilated_attn.so")
 DA_F32, DA_BF16 = 0, 1
 DA_HEAD_DIM = 64
 DA_MAX_PATTERNS = 8
+DA_NOALLOC_MAX_WORKSPACE_BYTES = 64 << 20
 
 ERROR_NAMES = {
     0: "DA_OK", -1: "DA_ERR_NULL", -2: "DA_ERR_SHAPE", -3: "DA_ERR_PATTERN", -4: "DA_ERR_DTYPE",
@@ -50,6 +51,7 @@ SIGNATURES = {
     "dilated_attn_qk_norm_bwd": ([_P] * 9 + [_I64, _I32, _I32, ctypes.c_float, _P, _SZ, _P],
                                  ctypes.c_int),
     "dilated_attn_fwd_onepass": (_FWD_ARGS[:-3] + [_P], ctypes.c_int),
+    "dilated_attn_fwd_noalloc": (_FWD_ARGS[:-3] + [_P], ctypes.c_int),
     "dilated_attn_fwd_qknorm": ([_P] * 7 + [ctypes.c_float, _P, _P, _I64, _I64, _I32, _I32, _I64,
                                            _P, _I32, _I32, _I32, ctypes.c_float, _P], ctypes.c_int),
     "dilated_attn_bwd_qknorm_workspace_bytes": ([_I64, _I64, _I32, _I32, _P, _I32, _I32,

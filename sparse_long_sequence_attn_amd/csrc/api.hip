@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "da_common.hpp"
 #include "dilated_attn.h"
@@ -221,11 +222,16 @@ int qkn_row_stride(const Plan& pl, int64_t given, int64_t* rsi) {
   return DA_OK;
 }
 
+// with_ws false: the tensors only (the workspace is checked once it is known)
 int check_buffers(const Plan& pl, const void* q, const void* k, const void* v, const void* out,
-                  const float* lse, const void* ws, size_t ws_bytes) {
+                  const float* lse, const void* ws, size_t ws_bytes, bool with_ws = true) {
   if (!q || !k || !v || !out || !lse) return DA_ERR_NULL;
-  if (pl.ws_bytes > 0 && !ws) return DA_ERR_WORKSPACE;
-  if (ws_bytes < pl.ws_bytes) return DA_ERR_WORKSPACE;
+  if (!with_ws) {
+    ws = nullptr;
+  } else {
+    if (pl.ws_bytes > 0 && !ws) return DA_ERR_WORKSPACE;
+    if (ws_bytes < pl.ws_bytes) return DA_ERR_WORKSPACE;
+  }
   auto mis = [](const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) != 0; };
   if (mis(q, 16) || mis(k, 16) || mis(v, 16) || mis(out, 16) || mis(lse, 4)) return DA_ERR_ALIGN;
   if (pl.ws_bytes > 0 && mis(ws, 256)) return DA_ERR_ALIGN;
@@ -283,6 +289,39 @@ int run_merge(const Plan& pl, void* out, float* lse, const void* ws, hipStream_t
   for (int i = 0; i < pl.np; ++i) m.pat[i] = pl.pat[i];
   const hipError_t e = da::launch_merge(m, pl.bf16, st);
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+// Workspace of the allocation-free forward entry point: one array per GPU,
+// held by the loaded code object until the process ends. Host code never
+// uses this name as an address (on the host it is only a stand-in for the
+// symbol); the per-device address comes from hipGetSymbolAddress.
+__device__ __attribute__((aligned(256))) unsigned char scratch[DA_NOALLOC_MAX_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device `stream` belongs to (the current
+// device for the null stream), looked up once per device with that device
+// current.
+int scratch_address(void* stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return DA_ERR_LAUNCH;
+  dev = cur;
+  if (stream && hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev) != hipSuccess)
+    return DA_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return DA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DA_ERR_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return DA_ERR_LAUNCH;
+    if (e != hipSuccess || !p) return DA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DA_OK;
 }
 
 enum Stage { kBoth = 3, kAttention = 1, kMerge = 2 };
@@ -606,6 +645,29 @@ int dilated_attn_fwd_onepass(const void* q, const void* k, const void* v, void* 
   const hipError_t e =
       da::launch_onepass(a, pl.causal, grid, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+int dilated_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int64_t B, int64_t N, int32_t H, int32_t Dh,
+                             const da_pattern* patterns, int32_t n_patterns, int32_t causal,
+                             int32_t dtype, float scale, void* stream) {
+  Plan pl;
+  int rc = make_plan(B, N, H, Dh, patterns, n_patterns, causal, dtype, scale, &pl);
+  if (rc != DA_OK || pl.empty) return rc;
+  if (pl.ws_bytes > DA_NOALLOC_MAX_WORKSPACE_BYTES) return DA_ERR_WORKSPACE;
+  rc = check_buffers(pl, q, k, v, out, lse, nullptr, 0, false);
+  if (rc != DA_OK) return rc;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    rc = scratch_address(stream, &ws);
+    if (rc != DA_OK) return rc;
+    rc = check_buffers(pl, q, k, v, out, lse, ws, DA_NOALLOC_MAX_WORKSPACE_BYTES);
+    if (rc != DA_OK) return rc;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  rc = run_attention(pl, q, k, v, out, lse, ws, st);
+  if (rc != DA_OK) return rc;
+  return run_merge(pl, out, lse, ws, st);
 }
 
 int dilated_attn_fwd_qknorm(const void* xq, const void* xk, const void* v, const void* gain_q,

@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = header_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_native.SIGNATURES)
@@ -54,6 +54,8 @@ def test_binding_constants_match_header():
     text = open(HEADER).read()
     assert int(re.search(r"#define DA_MAX_PATTERNS (\d+)", text)[1]) == _native.DA_MAX_PATTERNS
     assert int(re.search(r"#define DA_HEAD_DIM (\d+)", text)[1]) == _native.DA_HEAD_DIM
+    m = re.search(r"#define DA_NOALLOC_MAX_WORKSPACE_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert (int(m[1]) << int(m[2])) == _native.DA_NOALLOC_MAX_WORKSPACE_BYTES
     assert int(re.search(r"#define DA_VERSION (\d+)", text)[1]) == _native.version()
 
 
@@ -402,3 +404,42 @@ def test_onepass_invalid_calls_rejected(lib, kwargs, code):
 
 def test_onepass_empty_problem_is_a_no_op(lib):
     assert onepass(lib, B=0, q=None, k=None, v=None, out=None, lse=None) == 0
+
+
+def noalloc(lib, q=Q, k=K, v=V, out=OUT, lse=LSE, B=1, N=64, H=4, Dh=64, pats=((16, 2), (32, 4)),
+            causal=1, dtype=_native.DA_BF16, scale=0.0):
+    arr = _native.pattern_array(pats)
+    return lib.dilated_attn_fwd_noalloc(q, k, v, out, lse, B, N, H, Dh, arr, len(pats), causal,
+                                        dtype, scale, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(N=60), -2), (dict(B=-1), -2),
+    (dict(pats=((16, 0),)), -3), (dict(pats=((16, 2),) * 9), -3),
+    (dict(dtype=2), -4), (dict(Dh=32), -5),
+    (dict(q=Q + 8), -7), (dict(lse=LSE + 2), -7),
+    (dict(out=Q), -8), (dict(lse=K + 64), -8), (dict(out=LSE), -8),
+    (dict(causal=2), -9), (dict(scale=math.nan), -9),
+])
+def test_noalloc_invalid_calls_rejected(lib, kwargs, code):
+    assert noalloc(lib, **kwargs) == code
+
+
+def test_noalloc_rejects_workspaces_beyond_its_array(lib):
+    """A problem whose workspace exceeds the library's array is refused before
+    anything touches HIP; one just inside it only fails on the fake pointers'
+    overlap, also before any HIP call."""
+    limit = _native.DA_NOALLOC_MAX_WORKSPACE_BYTES
+    pats = ((64, 1), (128, 2))
+    big = 1
+    while _native.workspace_bytes(1, 1 << big, 16, 64, pats, _native.DA_BF16) <= limit:
+        big += 1
+    N = 1 << big
+    assert _native.workspace_bytes(1, N, 16, 64, pats, _native.DA_BF16) > limit
+    assert noalloc(lib, N=N, H=16, pats=pats) == -6
+    assert noalloc(lib, N=N, H=16, pats=pats, out=Q) == -6  # the size is checked first
+
+
+def test_noalloc_empty_problem_is_a_no_op(lib):
+    assert noalloc(lib, B=0, q=None, k=None, v=None, out=None, lse=None) == 0
