@@ -84,7 +84,7 @@ int tile_order(const Plan* pl, int bm, TileOrder* to) {
 void sorted_patterns(const Plan& pl, const TileOrder& to, PatDev* dst, int64_t* unit_start) {
   for (int j = 0; j < pl.np; ++j) {
     dst[j] = pl.pat[to.order[j]];
-    dst[j].ntile = to.ntile[to.order[j]];
+    da::set_tile_divisors(&dst[j], to.ntile[to.order[j]]);
   }
   for (int j = 0; j <= pl.np; ++j) unit_start[j] = to.unit_start[j];
 }
@@ -262,6 +262,7 @@ int run_attention(const Plan& pl, const void* q, const void* k, const void* v, v
   a.H = pl.H;
   a.np = pl.np;
   a.sl2 = pl.sl2;
+  a.h_div = da::make_fastdiv((uint32_t)pl.H);
   sorted_patterns(pl, pl.fwd, a.pat, a.unit_start);
   hipError_t e;
   a.in_rs = in_rs ? in_rs : (int64_t)pl.H * DA_HEAD_DIM;
@@ -506,6 +507,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   a.np = pl.np;
   a.sl2 = pl.sl2;
   a.scale = pl.scale;
+  a.h_div = da::make_fastdiv((uint32_t)pl.H);
   sorted_patterns(pl, pl.bwd, a.pat, a.unit_start);
   for (int j = 0; j < pl.np; ++j) a.pat[j].po_off = pl.bwd_po_off[pl.bwd.order[j]];
   float* const qkn_part =

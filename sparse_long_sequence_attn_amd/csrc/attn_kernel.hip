@@ -57,42 +57,18 @@ struct Tile {
 
 // Block id -> tile (see AttnArgs for the order). Returns false for the
 // padding blocks of XCDs whose list is shorter than the longest one.
-__device__ inline bool decode_tile(const AttnArgs& a, int64_t id, Tile* t) {
-  const int32_t x = (int32_t)(id % kXcds);
-  int64_t slot = id / kXcds;
-  for (int p = 0; p < a.np; ++p) {
-    const int64_t u0 = a.unit_start[p], u1 = a.unit_start[p + 1];
-    // first unit of this pattern dealt to XCD x, and how many it gets
-    const int64_t first = u0 + (((x - u0) % kXcds) + kXcds) % kXcds;
-    const int64_t cnt = first < u1 ? (u1 - first + kXcds - 1) / kXcds : 0;
-    const int64_t nt = a.pat[p].ntile;
-    if (slot < cnt * nt) {
-      // groups of G units (their key/value rows fill about an XCD's L2),
-      // heaviest tiles of the group first; the last pattern's units form
-      // one group, so the XCD's list ends with its shortest tiles
-      const int64_t G = p == a.np - 1 ? (cnt > 0 ? cnt : 1) : 4;
-      const int64_t gfull = cnt / G;
-      int64_t gi = slot / (G * nt), gsz = G;
-      if (gi >= gfull) {
-        gi = gfull;
-        gsz = cnt - gfull * G;
-      }
-      const int64_t r0 = slot - gi * G * nt;
-      const int64_t k = r0 / gsz;
-      const int64_t lu = gi * G + r0 % gsz;
-      const int64_t rem = first + lu * kXcds - u0;  // unit index inside the pattern
-      const int64_t nseg = a.pat[p].nseg;
-      t->seg = rem % nseg;
-      const int64_t bh = rem / nseg;
-      t->h = (int32_t)(bh % a.H);
-      t->b = bh / a.H;
-      t->p = p;
-      t->qt = (int32_t)(nt - 1 - k);
-      return true;
-    }
-    slot -= cnt * nt;
-  }
-  return false;
+__device__ inline bool decode_tile(const AttnArgs& a, uint32_t id, Tile* t) {
+  int32_t p;
+  uint32_t unit, rank;
+  if (!decode_order(a, id, &p, &unit, &rank)) return false;
+  const uint32_t bh = fdiv(unit, a.pat[p].nseg_div);
+  t->seg = unit - bh * (uint32_t)a.pat[p].nseg;
+  const uint32_t b = fdiv(bh, a.h_div);
+  t->h = (int32_t)(bh - b * (uint32_t)a.H);
+  t->b = b;
+  t->p = p;
+  t->qt = (int32_t)((uint32_t)a.pat[p].ntile - 1u - rank);
+  return true;
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -532,61 +508,99 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
       }
     }
 
-    // Lazy rescaling: a row's running max (log2 domain) only moves when the
-    // tile raises it by more than 8, so p = 2^(s - m_run) stays below 2^8
-    // and most tiles skip rescaling O and l.
-    float mt[QB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    // the row max of the tile (log2 domain), both lane halves
+    auto tile_max = [&](int qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, S[kb][qb][v]);
-      mt[qb] = pair_max(mx) * sl2;
-      grow = grow || (mt[qb] > m_run[qb] + 8.f);
-    }
-    if (!started) {
-      // first tile: O and l are still zero, only the max is set
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) m_run[qb] = mt[qb];
-      started = true;
-    } else if (__ballot(grow) != 0) {
+      return pair_max(mx) * sl2;
+    };
+    if constexpr (!BF) {
+      // Lazy rescaling: a row's running max (log2 domain) only moves when the
+      // tile raises it by more than 8, so p = 2^(s - m_run) stays below 2^8
+      // and most tiles skip rescaling O and l.
+      float mt[QB];
+      bool grow = false;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m_run[qb], mt[qb]);
-        const float alpha = exp2_fast(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+        mt[qb] = tile_max(qb);
+        grow = grow || (mt[qb] > m_run[qb] + 8.f);
+      }
+      if (!started) {
+        // first tile: O and l are still zero, only the max is set
 #pragma unroll
-        for (int db = 0; db < 2; ++db) O[db][qb] *= alpha;
+        for (int qb = 0; qb < QB; ++qb) m_run[qb] = mt[qb];
+        started = true;
+      } else if (__ballot(grow) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = fmaxf(m_run[qb], mt[qb]);
+          const float alpha = exp2_fast(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 2; ++db) O[db][qb] *= alpha;
+        }
       }
     }
 
     if constexpr (BF) {
-      // P rounded to bf16 once: the same packed registers feed the PV MFMA
-      // and the row sum
-      u32x4 pw[QB][2 * KB];
+      // The first tile of a row sets its running max m (log2 domain); later
+      // tiles form p = 2^(s sl2 - m) against it without a max of their own
+      // (p may exceed 1: fp32 sums and bf16 probabilities carry that
+      // exactly as well). Only when a tile's sum over one lane's keys
+      // reaches 2^32 (or overflows) is the tile redone against
+      // max(m, its max), with O and l rescaled first; O then stays below
+      // 2^53 times the largest |v|. P is rounded to bf16 once: the same
+      // packed registers feed the PV MFMA and the row sum.
+      if (!started) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float lsum = 0.f;
-#pragma unroll
-        for (int c = 0; c < 2 * KB; ++c) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = exp2_fast(fmaf(S[c >> 1][qb][8 * (c & 1) + e], sl2, -m_run[qb]));
-            const float p1 = exp2_fast(fmaf(S[c >> 1][qb][8 * (c & 1) + e + 1], sl2, -m_run[qb]));
-            bf16x2 pr;
-            pr[0] = (__bf16)p0;
-            pr[1] = (__bf16)p1;
-            pw[qb][c][e >> 1] = __builtin_bit_cast(uint32_t, pr);
-            const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, lsum, false);
-          }
-        }
-        l_run[qb] += lsum;
+        for (int qb = 0; qb < QB; ++qb) m_run[qb] = tile_max(qb);
+        started = true;
       }
+      u32x4 pw[QB][2 * KB];
+      float lsum[QB];
+      auto form_p = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float ls[2] = {0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 2 * KB; ++c) {
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const float p0 = exp2_fast(fmaf(S[c >> 1][qb][8 * (c & 1) + e], sl2, -m_run[qb]));
+              const float p1 = exp2_fast(fmaf(S[c >> 1][qb][8 * (c & 1) + e + 1], sl2, -m_run[qb]));
+              bf16x2 pr;
+              pr[0] = (__bf16)p0;
+              pr[1] = (__bf16)p1;
+              pw[qb][c][e >> 1] = __builtin_bit_cast(uint32_t, pr);
+              const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+              ls[c & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[c & 1], false);
+            }
+          }
+          lsum[qb] = ls[0] + ls[1];
+        }
+      };
+      form_p();
+      bool over = false;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) over = over || !(lsum[qb] < 4294967296.f);
+      if (__ballot(over) != 0) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const float m_new = fmaxf(m_run[qb], tile_max(qb));
+          const float alpha = exp2_fast(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 2; ++db) O[db][qb] *= alpha;
+        }
+        form_p();
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
       // A operand of O^T += V^T P^T for (dims db*32.., keys 16c..16c+15):
       // lane (n, hh) needs V[16c + 8h + 4hh + j][db*32 + n], j = 0..3, for
       // h = 0, 1. In 16-lane group g (n = 16(g&1) + i, hh = g>>1) lane m

@@ -16,6 +16,7 @@ namespace da {
 // order; row index ((b * H + h) * nseg + seg) * lmax + m). Rows that exactly
 // one pattern gathers bypass them and are written to dq / dk / dv directly.
 struct BwdArgs {
+  FastDiv h_div;      // division by H
   const void* q;
   const void* k;
   const void* v;

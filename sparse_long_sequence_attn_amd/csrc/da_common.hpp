@@ -47,9 +47,13 @@ struct PatDev {
   int32_t r;       // dilation rate
   int32_t lmax;    // ceil(wp / r): rows gathered by a head with offset 0
   int32_t ntile;   // query tiles per segment: ceil(lmax / BM)
-  int32_t pad_;
+  int32_t cnt_hi;  // units an XCD gets at most: ceil(units / kXcds) (set per launch)
   FastDiv wp_div;  // division by wp
   FastDiv r_div;   // division by r
+  // set per launch by the host for the tile order below
+  FastDiv nseg_div;    // division by nseg
+  FastDiv grp_div;     // division by 4 * ntile (a group of 4 units' tiles)
+  FastDiv cnt_div[2];  // division by floor and ceil of units / kXcds
 };
 
 // Attention launch. Tiles of all patterns share one grid. Block ids are
@@ -66,6 +70,7 @@ struct PatDev {
 constexpr int kXcds = 8;
 
 struct AttnArgs {
+  FastDiv h_div;   // division by H
   const void* q;
   const void* k;
   const void* v;
@@ -128,6 +133,81 @@ struct MergeArgs {
   int32_t np;
   PatDev pat[kMaxPat];  // caller's order (any order gives the same merge)
 };
+
+// Host side of the tile order: the divisors the device decode below uses,
+// for a pattern with `ntile` tiles per unit in a launch's order.
+inline void set_tile_divisors(PatDev* p, int32_t ntile) {
+  p->ntile = ntile;
+  const uint32_t lo = (uint32_t)(p->units / kXcds), hi = (uint32_t)((p->units + kXcds - 1) / kXcds);
+  p->cnt_hi = (int32_t)hi;
+  p->nseg_div = make_fastdiv((uint32_t)p->nseg);
+  p->grp_div = make_fastdiv(4u * (uint32_t)ntile);
+  p->cnt_div[0] = make_fastdiv(lo > 0 ? lo : 1u);
+  p->cnt_div[1] = make_fastdiv(hi > 0 ? hi : 1u);
+}
+
+#if defined(__HIPCC__)
+// a / b for a < 2^22 and b >= 1: the float reciprocal's quotient is off by
+// at most one there, and one correction each way makes it exact.
+__device__ inline uint32_t udiv_small(uint32_t a, uint32_t b) {
+  uint32_t q = (uint32_t)((float)a * __builtin_amdgcn_rcpf((float)b));
+  const int32_t r = (int32_t)(a - q * b);
+  if (r < 0) --q;
+  else if ((uint32_t)r >= b) ++q;
+  return q;
+}
+
+// Block id -> (pattern, unit, tile rank) of the launch order described at
+// AttnArgs: ids are dealt to the XCDs round-robin (id mod kXcds); each XCD
+// gets its share of every pattern's units (patterns sorted by tiles per
+// unit) and walks them in groups of 4 units, the group's heaviest tiles
+// first, the last pattern's units forming one group. Returns false for the
+// padding ids of XCDs whose list is shorter than the longest one. All
+// quantities are below 2^31 (the host keeps the grid so), so the decode is
+// 32-bit: shifts, multiply-high divisions by divisors the host prepared
+// (set_tile_divisors) and small float-reciprocal divisions. `rank` is the
+// tile's position in its unit's heaviest-first order; `unit` is
+// ((b * H) + h) * nseg + seg.
+template <class Args>
+__device__ inline bool decode_order(const Args& a, uint32_t id, int32_t* pat, uint32_t* unit,
+                                    uint32_t* rank) {
+  static_assert(kXcds == 8, "XCD decode written for 8 XCDs");
+  const uint32_t x = id & 7u;
+  uint32_t slot = id >> 3;
+  for (int p = 0; p < a.np; ++p) {
+    const PatDev& P = a.pat[p];
+    const uint32_t u0 = (uint32_t)a.unit_start[p];
+    const uint32_t units = (uint32_t)a.unit_start[p + 1] - u0;
+    const uint32_t extra = (x - u0) & 7u;  // this XCD's first unit is u0 + extra
+    const uint32_t cnt = extra < units ? (units - extra + 7u) >> 3 : 0u;
+    const uint32_t nt = (uint32_t)P.ntile;
+    const uint32_t ntot = cnt * nt;
+    if (slot < ntot) {
+      uint32_t k, lu;
+      if (p == a.np - 1) {  // one group of all cnt units
+        k = fdiv(slot, P.cnt_div[cnt == (uint32_t)P.cnt_hi ? 1 : 0]);
+        lu = slot - k * cnt;
+      } else {
+        const uint32_t gfull = cnt >> 2;
+        uint32_t gi = fdiv(slot, P.grp_div), gsz = 4u;
+        if (gi >= gfull) {
+          gi = gfull;
+          gsz = cnt - 4u * gfull;
+        }
+        const uint32_t r0 = slot - gi * 4u * nt;
+        k = udiv_small(r0, gsz);
+        lu = 4u * gi + (r0 - k * gsz);
+      }
+      *pat = p;
+      *unit = extra + lu * 8u;
+      *rank = k;
+      return true;
+    }
+    slot -= ntot;
+  }
+  return false;
+}
+#endif
 
 // ---------------------------------------------------------------- index maps
 

@@ -155,37 +155,17 @@ struct UnitTile {
 // XCDs whose list is shorter than the longest one.
 template <bool LAST_FIRST, class Args>
 __device__ inline bool decode_unit_tile(const Args& a, int64_t id, UnitTile* t) {
-  const int32_t x = (int32_t)(id % kXcds);
-  int64_t slot = id / kXcds;
-  for (int p = 0; p < a.np; ++p) {
-    const int64_t u0 = a.unit_start[p], u1 = a.unit_start[p + 1];
-    const int64_t first = u0 + (((x - u0) % kXcds) + kXcds) % kXcds;
-    const int64_t cnt = first < u1 ? (u1 - first + kXcds - 1) / kXcds : 0;
-    const int64_t nt = a.pat[p].ntile;
-    if (slot < cnt * nt) {
-      const int64_t G = p == a.np - 1 ? (cnt > 0 ? cnt : 1) : 4;
-      const int64_t gfull = cnt / G;
-      int64_t gi = slot / (G * nt), gsz = G;
-      if (gi >= gfull) {
-        gi = gfull;
-        gsz = cnt - gfull * G;
-      }
-      const int64_t r0 = slot - gi * G * nt;
-      const int32_t k = (int32_t)(r0 / gsz);
-      const int64_t lu = gi * G + r0 % gsz;
-      const int64_t rem = first + lu * kXcds - u0;
-      const int64_t nseg = a.pat[p].nseg;
-      t->seg = rem % nseg;
-      const int64_t bh = rem / nseg;
-      t->h = (int32_t)(bh % a.H);
-      t->b = bh / a.H;
-      t->p = p;
-      t->tile = LAST_FIRST ? (int32_t)(nt - 1 - k) : k;
-      return true;
-    }
-    slot -= cnt * nt;
-  }
-  return false;
+  int32_t p;
+  uint32_t unit, rank;
+  if (!decode_order(a, (uint32_t)id, &p, &unit, &rank)) return false;
+  const uint32_t bh = fdiv(unit, a.pat[p].nseg_div);
+  t->seg = unit - bh * (uint32_t)a.pat[p].nseg;
+  const uint32_t b = fdiv(bh, a.h_div);
+  t->h = (int32_t)(bh - b * (uint32_t)a.H);
+  t->b = b;
+  t->p = p;
+  t->tile = LAST_FIRST ? (int32_t)((uint32_t)a.pat[p].ntile - 1u - rank) : (int32_t)rank;
+  return true;
 }
 
 // Number of patterns that gather position t for head h.

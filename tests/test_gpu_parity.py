@@ -107,6 +107,25 @@ def test_softmax_range_with_boosted_keys(torch_cuda):
     compare(out_g, lse_g, out_o, lse_o, "bf16", "boosted keys")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_scores_growing_far_beyond_the_first_block(torch_cuda, causal):
+    """Keys in the second half of every 1024-row segment are 64 times larger
+    (exact in bf16), so a row's scores jump, block after block, far past the
+    running max its first blocks set (by hundreds in the log2 domain): the
+    kernels must rebase the running max instead of overflowing."""
+    q, k, v = random_inputs(1, 2048, 4, 64, "f32", seed=77)
+    for s0 in (0, 1024):
+        k[:, s0 + 512:s0 + 1024] *= np.float32(64.0)
+        k[:, s0 + 768:s0 + 1024] *= np.float32(4.0)
+    from sparse_long_sequence_attn_amd.workloads import bf16_round_bits
+    q, k, v = (bf16_round_bits(x) for x in (q, k, v))
+    pats = [(1024, 1), (2048, 2)]
+    out_o, lse_o = oracle.fwd(q, k, v, pats, causal=causal)
+    out_g, lse_g = run_gpu(torch_cuda, q, k, v, pats, causal=causal)
+    assert np.isfinite(out_g).all()
+    compare(out_g, lse_g, out_o, lse_o, "bf16", f"growing scores causal={causal}")
+
+
 # ---------------------------------------------------------------- the five workloads
 
 @pytest.mark.parametrize("name", [
