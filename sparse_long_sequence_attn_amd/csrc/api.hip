@@ -84,7 +84,7 @@ int tile_order(const Plan* pl, int bm, TileOrder* to) {
 void sorted_patterns(const Plan& pl, const TileOrder& to, PatDev* dst, int64_t* unit_start) {
   for (int j = 0; j < pl.np; ++j) {
     dst[j] = pl.pat[to.order[j]];
-    da::set_tile_divisors(&dst[j], to.ntile[to.order[j]]);
+    da::set_tile_divisors(&dst[j], to.ntile[to.order[j]], j == pl.np - 1);
   }
   for (int j = 0; j <= pl.np; ++j) unit_start[j] = to.unit_start[j];
 }

@@ -47,13 +47,13 @@ struct PatDev {
   int32_t r;       // dilation rate
   int32_t lmax;    // ceil(wp / r): rows gathered by a head with offset 0
   int32_t ntile;   // query tiles per segment: ceil(lmax / BM)
-  int32_t cnt_hi;  // units an XCD gets at most: ceil(units / kXcds) (set per launch)
+  int32_t group;   // units per group of the tile order (set per launch)
   FastDiv wp_div;  // division by wp
   FastDiv r_div;   // division by r
   // set per launch by the host for the tile order below
-  FastDiv nseg_div;    // division by nseg
-  FastDiv grp_div;     // division by 4 * ntile (a group of 4 units' tiles)
-  FastDiv cnt_div[2];  // division by floor and ceil of units / kXcds
+  FastDiv nseg_div;  // division by nseg
+  FastDiv g_div;     // division by group
+  FastDiv grp_div;   // division by group * ntile (one group's tiles)
 };
 
 // Attention launch. Tiles of all patterns share one grid. Block ids are
@@ -61,10 +61,11 @@ struct PatDev {
 // out per XCD: each XCD gets its share of every pattern's (batch, head,
 // segment) units and walks them in groups of 4 units, heaviest tiles of the
 // group first (the last query tile of each unit, then the one before it,
-// and so on); the last pattern's units form one group. A group's key/value
-// rows about fill the XCD's L2, and the list ends with its shortest tiles,
-// so the XCD's workgroup slots drain together instead of waiting on the
-// long tiles of the final units. Patterns are
+// and so on); the last pattern's groups are larger (up to what its units'
+// key/value rows need of the XCD's 4 MiB L2). A group's key/value rows
+// about fill the L2, and the list ends with its shortest tiles, so the
+// XCD's workgroup slots drain together instead of waiting on the long
+// tiles of the final units. Patterns are
 // stored sorted by ntile (descending); units are handed to XCDs round-robin
 // in that order.
 constexpr int kXcds = 8;
@@ -134,16 +135,24 @@ struct MergeArgs {
   PatDev pat[kMaxPat];  // caller's order (any order gives the same merge)
 };
 
-// Host side of the tile order: the divisors the device decode below uses,
-// for a pattern with `ntile` tiles per unit in a launch's order.
-inline void set_tile_divisors(PatDev* p, int32_t ntile) {
+// Host side of the tile order: the group size and the divisors the device
+// decode below uses, for a pattern with `ntile` tiles per unit in a
+// launch's order. Groups hold 4 units; the last pattern's group is larger,
+// up to what fills an XCD's 4 MiB L2 with the units' key and value rows
+// (4 to 16 units), so that the XCD's list ends with its shortest tiles
+// without sending more units' rows through the L2 at once than it holds.
+inline void set_tile_divisors(PatDev* p, int32_t ntile, bool last) {
   p->ntile = ntile;
-  const uint32_t lo = (uint32_t)(p->units / kXcds), hi = (uint32_t)((p->units + kXcds - 1) / kXcds);
-  p->cnt_hi = (int32_t)hi;
+  int32_t g = 4;
+  if (last) {
+    const int64_t unit_bytes = (int64_t)p->lmax * kDh * 2 * 2;  // bf16 K and V rows
+    const int64_t fit = ((int64_t)4 << 20) / (unit_bytes > 0 ? unit_bytes : 1);
+    g = (int32_t)(fit < 4 ? 4 : fit > 16 ? 16 : fit);
+  }
+  p->group = g;
   p->nseg_div = make_fastdiv((uint32_t)p->nseg);
-  p->grp_div = make_fastdiv(4u * (uint32_t)ntile);
-  p->cnt_div[0] = make_fastdiv(lo > 0 ? lo : 1u);
-  p->cnt_div[1] = make_fastdiv(hi > 0 ? hi : 1u);
+  p->g_div = make_fastdiv((uint32_t)g);
+  p->grp_div = make_fastdiv((uint32_t)g * (uint32_t)ntile);
 }
 
 #if defined(__HIPCC__)
@@ -160,8 +169,8 @@ __device__ inline uint32_t udiv_small(uint32_t a, uint32_t b) {
 // Block id -> (pattern, unit, tile rank) of the launch order described at
 // AttnArgs: ids are dealt to the XCDs round-robin (id mod kXcds); each XCD
 // gets its share of every pattern's units (patterns sorted by tiles per
-// unit) and walks them in groups of 4 units, the group's heaviest tiles
-// first, the last pattern's units forming one group. Returns false for the
+// unit) and walks them in groups (PatDev::group units), the group's
+// heaviest tiles first. Returns false for the
 // padding ids of XCDs whose list is shorter than the longest one. All
 // quantities are below 2^31 (the host keeps the grid so), so the decode is
 // 32-bit: shifts, multiply-high divisions by divisors the host prepared
@@ -183,23 +192,18 @@ __device__ inline bool decode_order(const Args& a, uint32_t id, int32_t* pat, ui
     const uint32_t nt = (uint32_t)P.ntile;
     const uint32_t ntot = cnt * nt;
     if (slot < ntot) {
-      uint32_t k, lu;
-      if (p == a.np - 1) {  // one group of all cnt units
-        k = fdiv(slot, P.cnt_div[cnt == (uint32_t)P.cnt_hi ? 1 : 0]);
-        lu = slot - k * cnt;
-      } else {
-        const uint32_t gfull = cnt >> 2;
-        uint32_t gi = fdiv(slot, P.grp_div), gsz = 4u;
-        if (gi >= gfull) {
-          gi = gfull;
-          gsz = cnt - 4u * gfull;
-        }
-        const uint32_t r0 = slot - gi * 4u * nt;
-        k = udiv_small(r0, gsz);
-        lu = 4u * gi + (r0 - k * gsz);
+      // groups of G units; the last one holds the remaining cnt mod G
+      const uint32_t G = (uint32_t)P.group;
+      const uint32_t gfull = fdiv(cnt, P.g_div);
+      uint32_t gi = fdiv(slot, P.grp_div), gsz = G;
+      if (gi >= gfull) {
+        gi = gfull;
+        gsz = cnt - G * gfull;
       }
+      const uint32_t r0 = slot - gi * G * nt;  // below G * ntile < 2^21
+      const uint32_t k = udiv_small(r0, gsz);
       *pat = p;
-      *unit = extra + lu * 8u;
+      *unit = extra + (G * gi + (r0 - k * gsz)) * 8u;
       *rank = k;
       return true;
     }

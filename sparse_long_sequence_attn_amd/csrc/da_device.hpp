@@ -148,8 +148,9 @@ struct UnitTile {
 // Block id -> tile. Block ids are dealt to the XCDs round-robin (id mod
 // kXcds); each XCD walks its share of every pattern's units in groups of 4
 // units (their rows about fill the XCD's L2), the heaviest tiles of the
-// group first; the last pattern's units form one group, so the XCD's list
-// ends with its shortest tiles and its workgroup slots drain together. The
+// group first; the last pattern's groups are larger (as many units as fill
+// the L2), so the XCD's list ends with its shortest tiles and its workgroup
+// slots drain together (decode_order). The
 // heaviest tile of a unit is its last one (LAST_FIRST) or its first one,
 // whichever carries the most work. Returns false for the padding blocks of
 // XCDs whose list is shorter than the longest one.
