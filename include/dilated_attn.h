@@ -36,8 +36,16 @@
  * is the default stream) and return without synchronising. Faults during
  * execution surface at the caller's next synchronisation.
  *
- * Errors: every call validates all arguments before launching anything; on
- * a non-zero return nothing was launched and nothing was written.
+ * Errors: every call validates all arguments before launching anything.
+ * A non-zero return other than DA_ERR_LAUNCH means nothing was launched and
+ * nothing was written. DA_ERR_LAUNCH (the runtime rejected a launch) can
+ * follow kernels of the same call that were already enqueued on the stream
+ * (an attention launch before a failed merge launch, earlier backward
+ * stages); the outputs are then undefined.
+ *
+ * Inputs are not checked for finiteness. Elements of q, k, v are expected
+ * to be finite: a NaN or infinity reaches the rows whose softmax it enters
+ * with unspecified values (the kernels take maxima without NaN ordering).
  */
 #ifndef DILATED_ATTN_H
 #define DILATED_ATTN_H
@@ -87,14 +95,22 @@ enum {
 /* Bytes of device workspace dilated_attn_fwd needs for this problem (0 for
  * a single pattern, whose kernel writes out and lse directly). For two or
  * more patterns it holds each pattern's per-row partial output (float, Dh
- * per gathered row) and log-sum-exp before the merge. Writes *bytes and
- * returns DA_OK, or an error code for invalid arguments. */
+ * per gathered row) and log-sum-exp before the merge: the per-pattern
+ * results of the mixture of dilated patterns (dakule.com news page, "如何
+ * 做到？"; LONGNET blog, "LongNet's attention allocation principle") that
+ * the merge weighs by their softmax denominators. Writes *bytes and returns
+ * DA_OK, or an error code for invalid arguments. */
 int dilated_attn_workspace_bytes(int64_t B, int64_t N, int32_t H, int32_t Dh,
                                  const da_pattern* patterns, int32_t n_patterns, int32_t dtype,
                                  size_t* bytes);
 
-/* The whole forward pass: dilated attention for every pattern, then the
- * log-sum-exp merge. Writes every element of out and lse. causal is 0 or 1.
+/* The whole forward pass (LONGNET blog, "LongNet's attention allocation
+ * principle" and the multi-head paragraph after it; "LongNet论文精读" page,
+ * "Dilated Attention的工作原理", steps 1-4: segment, gather every r-th row
+ * from the head's offset, dense attention inside each sparsified segment,
+ * scatter back; dakule.com news page, "实验评估", for the mixture of
+ * patterns): dilated attention for every pattern, then the log-sum-exp
+ * merge. Writes every element of out and lse. causal is 0 or 1.
  * workspace: device memory of at least dilated_attn_workspace_bytes() bytes,
  * 256-byte aligned (may be NULL when that size is 0); its contents on entry
  * are ignored. Returns DA_OK or a DA_ERR_* code. */
@@ -313,14 +329,20 @@ int dilated_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* 
                              const da_pattern* patterns, int32_t n_patterns, int32_t causal,
                              int32_t dtype, float scale, void* stream);
 
-/* Test hook: the gather map the kernels use, written by a device kernel
- * through the same index function as the attention kernel.
- * dev_out: device int64 [N / min(w, N)][ceil(min(w, N) / r)], segment-major;
+/* Test hook: the gather map the kernels use (LONGNET blog, "LongNet's
+ * attention allocation principle" and the multi-head paragraph after it:
+ * segments of w tokens, every r-th token from the head's offset; "LongNet
+ * 论文精读" page, "Dilated Attention的工作原理", steps 1-2), written by a
+ * device kernel through the same index function as the attention kernel.
+ * shape: host int64[2], may be NULL; receives the map's shape
+ * {N / min(w, N), ceil(min(w, N) / r)} (segments, rows per segment of a head
+ * with offset 0). dev_out: device int64 array of that shape, segment-major;
  * entry [s][m] is the sequence position of gathered row m of segment s for
  * head h, or -1 where m >= L(h). cap is dev_out's length in elements and must
- * be at least that size. */
+ * be at least shape[0] * shape[1]. With dev_out NULL the call only fills
+ * shape (which must then be non-NULL) and launches nothing. */
 int dilated_attn_gather_map(int64_t N, int32_t H, da_pattern pattern, int32_t h, int64_t* dev_out,
-                            int64_t cap, void* stream);
+                            int64_t cap, int64_t* shape, void* stream);
 
 /* Test hook: the inverse map the merge kernel uses. dev_out: device int64
  * [N]; entry t is s * ceil(min(w, N) / r) + m when position t is gathered

@@ -225,29 +225,36 @@ def dilated_attn_merge_stage(prob, stream=None):
     prob.merge_stage(stream)
 
 
-def _map(fn_name, N, H, pattern, h, size, device):
+def gather_map(N, H, pattern, h, device="cuda"):
+    """Device dump of the gather map: int64 [nseg, lmax], -1 past L(h); the
+    library reports the shape."""
+    import ctypes
+
     import torch
 
-    out = torch.empty(max(size, 1), dtype=torch.int64, device=device)
     lib = load_library()
-    code = getattr(lib, fn_name)(int(N), int(H), _native.DaPattern(int(pattern[0]), int(pattern[1])),
-                                 int(h), out.data_ptr(), out.numel(),
-                                 torch.cuda.current_stream(out.device).cuda_stream)
-    _native.check(code, fn_name)
-    return out[:size]
-
-
-def gather_map(N, H, pattern, h, device="cuda"):
-    """Device dump of the gather map: int64 [nseg, lmax], -1 past L(h)."""
-    w, r = pattern
-    wp = min(int(w), int(N))
-    nseg, lmax = int(N) // wp, -(-wp // int(r))
-    return _map("dilated_attn_gather_map", N, H, pattern, h, nseg * lmax, device).view(nseg, lmax)
+    pat = _native.DaPattern(int(pattern[0]), int(pattern[1]))
+    shape = (ctypes.c_int64 * 2)()
+    code = lib.dilated_attn_gather_map(int(N), int(H), pat, int(h), None, 0, shape, None)
+    _native.check(code, "dilated_attn_gather_map")
+    nseg, lmax = int(shape[0]), int(shape[1])
+    out = torch.empty(max(nseg * lmax, 1), dtype=torch.int64, device=device)
+    code = lib.dilated_attn_gather_map(int(N), int(H), pat, int(h), out.data_ptr(), out.numel(),
+                                       None, torch.cuda.current_stream(out.device).cuda_stream)
+    _native.check(code, "dilated_attn_gather_map")
+    return out[:nseg * lmax].view(nseg, lmax)
 
 
 def coverage_map(N, H, pattern, h, device="cuda"):
     """Device dump of the inverse map: int64 [N], compact index or -1."""
-    return _map("dilated_attn_coverage_map", N, H, pattern, h, int(N), device)
+    import torch
+
+    out = torch.empty(max(int(N), 1), dtype=torch.int64, device=device)
+    code = load_library().dilated_attn_coverage_map(
+        int(N), int(H), _native.DaPattern(int(pattern[0]), int(pattern[1])), int(h),
+        out.data_ptr(), out.numel(), torch.cuda.current_stream(out.device).cuda_stream)
+    _native.check(code, "dilated_attn_coverage_map")
+    return out[:int(N)]
 
 
 def _check_rows(name, t, like):

@@ -59,7 +59,8 @@ SIGNATURES = {
     "dilated_attn_bwd_qknorm": ([_P] * 7 + [ctypes.c_float] + [_P] * 7 +
                                 [_I64, _I64, _I32, _I32, _I64, _P, _I32, _I32, _I32,
                                  ctypes.c_float, _P, _SZ, _P], ctypes.c_int),
-    "dilated_attn_gather_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, _P], ctypes.c_int),
+    "dilated_attn_gather_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, ctypes.POINTER(_I64), _P],
+                                ctypes.c_int),
     "dilated_attn_coverage_map": ([_I64, _I32, DaPattern, _I32, _P, _I64, _P], ctypes.c_int),
     "dilated_attn_strerror": ([ctypes.c_int], ctypes.c_char_p),
     "dilated_attn_version": ([], ctypes.c_int),

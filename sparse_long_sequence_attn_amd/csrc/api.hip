@@ -881,11 +881,15 @@ int dilated_attn_qk_norm_bwd(const void* xq, const void* xk, const void* dyq, co
 }
 
 int dilated_attn_gather_map(int64_t N, int32_t H, da_pattern pattern, int32_t h, int64_t* dev_out,
-                            int64_t cap, void* stream) {
+                            int64_t cap, int64_t* shape, void* stream) {
   PatDev p;
   int rc = map_pattern(N, H, pattern, h, &p);
   if (rc != DA_OK) return rc;
-  if (!dev_out) return DA_ERR_NULL;
+  if (shape) {
+    shape[0] = p.nseg;
+    shape[1] = p.lmax;
+  }
+  if (!dev_out) return shape ? DA_OK : DA_ERR_NULL;
   if (cap < p.nseg * p.lmax) return DA_ERR_ARG;
   if (((uintptr_t)dev_out & 7) != 0) return DA_ERR_ALIGN;
   const hipError_t e =

@@ -138,7 +138,12 @@ def test_workspace_bytes_errors(lib):
 
 @pytest.mark.parametrize("fn", ["dilated_attn_gather_map", "dilated_attn_coverage_map"])
 def test_map_hooks_validate(lib, fn):
-    f = getattr(lib, fn)
+    g = getattr(lib, fn)
+    if fn == "dilated_attn_gather_map":
+        def f(N, H, p, h, out, cap, stream):
+            return g(N, H, p, h, out, cap, None, stream)
+    else:
+        f = g
     p = _native.DaPattern(16, 2)
     assert f(64, 4, p, 0, None, 1 << 20, None) == -1
     assert f(60, 4, p, 0, A, 1 << 20, None) == -2
@@ -443,3 +448,17 @@ def test_noalloc_rejects_workspaces_beyond_its_array(lib):
 
 def test_noalloc_empty_problem_is_a_no_op(lib):
     assert noalloc(lib, B=0, q=None, k=None, v=None, out=None, lse=None) == 0
+
+
+@pytest.mark.parametrize("N,w,r", [(64, 16, 2), (96, 1000, 7), (32768, 16384, 6), (120, 40, 6),
+                                   (64, 64, 64)])
+def test_gather_map_shape_from_the_library(lib, N, w, r):
+    """The library reports the gather map's shape (segments, rows per
+    segment) without launching anything when no output buffer is given."""
+    shape = (ctypes.c_int64 * 2)()
+    assert lib.dilated_attn_gather_map(N, 4, _native.DaPattern(w, r), 0, None, 0, shape,
+                                       None) == 0
+    wp = min(w, N)
+    assert (shape[0], shape[1]) == (N // wp, -(-wp // r))
+    assert lib.dilated_attn_gather_map(N, 4, _native.DaPattern(w, r), 0, None, 0, None,
+                                       None) == -1
