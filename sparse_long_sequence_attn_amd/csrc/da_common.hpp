@@ -132,7 +132,18 @@ struct MergeArgs {
   int64_t N;
   int32_t H;
   int32_t np;
-  PatDev pat[kMaxPat];  // caller's order (any order gives the same merge)
+  PatDev pat[kMaxPat];  // caller's order (the order of the merge's sums)
+  // Row-enumerating launch (every position gathered by some pattern): the
+  // patterns are ranked by dilation (rank[i] of pat[i]); a row with two or
+  // more covering patterns is merged by the thread that enumerates it as a
+  // gathered row of its second covering pattern in rank order. Set by the
+  // launcher.
+  int32_t rank[kMaxPat];
+  int32_t nenum;                   // enumerated patterns
+  int32_t enum_pat[kMaxPat];       // their indices into pat
+  uint32_t enum_blk[kMaxPat + 1];  // first block of each
+  FastDiv enum_head_div[kMaxPat];  // division by nseg * lmax (slots per head)
+  FastDiv enum_lmax_div[kMaxPat];  // division by lmax
 };
 
 // Host side of the tile order: the group size and the divisors the device

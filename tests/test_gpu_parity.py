@@ -82,6 +82,11 @@ SMALL_CASES = [
     (2, 192, 7, [(192, 3), (192, 3)], True, None),        # a pattern listed twice
     (1, 512, 3, [(512, 1), (256, 2), (128, 4), (64, 8), (512, 8), (256, 1), (128, 2), (64, 1)],
      True, None),                                          # the maximum of 8 patterns
+    # merge over the rows that need it (some pattern has r = 1): patterns
+    # that do not nest, a duplicated dense pattern, rates that divide no w
+    (1, 600, 3, [(600, 1), (200, 3), (300, 2)], True, None),
+    (2, 256, 5, [(64, 1), (64, 1), (256, 4)], False, None),
+    (1, 1020, 4, [(1020, 3), (510, 1), (204, 5)], True, None),
 ]
 
 
