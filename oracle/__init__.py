@@ -87,7 +87,8 @@ class Oracle:
 
     def __init__(self, path=None):
         if path is None:
-            path = _build.LIB
+            # ORACLE_LIB names another build (the sanitized one)
+            path = os.environ.get("ORACLE_LIB") or _build.LIB
             if not os.path.exists(path):
                 _build.build(force=True)
         self.path = path

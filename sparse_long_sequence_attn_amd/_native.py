@@ -9,7 +9,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libdilated_attn.so")
+# DILATED_ATTN_LIB names another build of the same library (the
+# host-sanitized one, for CPU-only test runs); default: the in-tree build
+LIB_PATH = os.environ.get("DILATED_ATTN_LIB") or os.path.join(PKG, "libdilated_attn.so")
 
 DA_F32, DA_BF16 = 0, 1
 DA_HEAD_DIM = 64

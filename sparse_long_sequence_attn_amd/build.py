@@ -13,7 +13,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdilated_attn.so")
+# Host code under AddressSanitizer and UndefinedBehaviorSanitizer (device code
+# unchanged): for CPU-only test runs with clang's ASan runtime preloaded.
+LIB_ASAN = os.path.join(PKG, "libdilated_attn_asan.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 SOURCES = ["api.hip", "attn_kernel.hip", "merge_kernel.hip", "bwd_kernel.hip",
            "qknorm_kernel.hip"]
 HEADERS = ["da_common.hpp", "kernels.hpp"]
@@ -36,9 +41,11 @@ FLAGS = [
 EXTRA = {"attn_kernel.hip": ["-fno-honor-nans"]}
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, sanitize=False):
+    sub = os.path.join(BUILD_DIR, "asan") if sanitize else BUILD_DIR
+    obj = os.path.join(sub, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + (SAN_FLAGS if sanitize else []) + [
+        "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -47,19 +54,22 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link the shared library."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link the shared library
+    (with sanitize: the host-sanitized copy, LIB_ASAN)."""
+    os.makedirs(os.path.join(BUILD_DIR, "asan") if sanitize else BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
+    lib = LIB_ASAN if sanitize else LIB
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + (
+        SAN_FLAGS if sanitize else []) + objs
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -102,7 +102,10 @@ def _weight_grad(dy2, x2):
     GEMM over R = B * N rows leaves most of the chip idle (a 512 x 512 output
     is only a few dozen tiles), so long R is split into 32 chunks, one
     batched GEMM computes the chunk products (left operand a transposed view,
-    right operand contiguous) and their float32 sum is rounded once."""
+    right operand contiguous). Each chunk product leaves the GEMM rounded to
+    the operands' dtype (its accumulation is float32); the 32 chunks are then
+    summed in float32 and rounded once more, so a bf16 gradient carries two
+    roundings instead of one."""
     R = dy2.shape[0]
     S = 32
     if R % S == 0 and R // S >= 2048:
