@@ -77,9 +77,34 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w, heads):
+def parity_figures(out_gpu, lse_gpu, out_o, lse_o):
+    """Max-abs errors of the GPU result against the oracle's on the same
+    elements, the output error in units of the bf16 spacing at the oracle's
+    value (2^(floor(log2 |x|) - 7), with |x| floored at 1/16 so that values
+    near zero are judged at a fixed absolute scale), and how many oracle
+    values have |x| >= 4, where one bf16 spacing (2^-5) already exceeds
+    2e-2."""
+    import numpy as np
+
+    d = np.abs(out_gpu - out_o)
+    mag = np.maximum(np.abs(out_o), 1.0 / 16)
+    spacing = np.exp2(np.floor(np.log2(mag)) - 7)
+    fin = np.isfinite(lse_o)
+    return {
+        "max_abs_err_out": float(d.max()),
+        "max_err_out_bf16_spacings_min_x_1_16": float((d / spacing).max()),
+        "count_abs_oracle_ge_4": int((np.abs(out_o) >= 4).sum()),
+        "max_abs_err_lse": float(np.abs(lse_gpu[fin] - lse_o[fin]).max()) if fin.any() else 0.0,
+        "lse_inf_match": bool(np.array_equal(np.isfinite(lse_gpu), fin)),
+        "elements_compared": int(d.size),
+    }
+
+
+def cpu_baseline(w, heads, out_gpu=None, lse_gpu=None):
     """The oracle (as it stands) on the first `heads` heads of the workload:
-    heads are independent, so the full workload costs H / heads times as much."""
+    heads are independent, so the full workload costs H / heads times as much.
+    With the GPU's out and lse (torch tensors) its result is also compared
+    with the oracle's on those heads."""
     import numpy as np
 
     import oracle
@@ -88,9 +113,14 @@ def cpu_baseline(w, heads):
     q, k, v = host_inputs(w)
     q, k, v = (np.ascontiguousarray(x[:, :, :heads]) for x in (q, k, v))
     t0 = time.perf_counter()
-    oracle.fwd(q, k, v, w.patterns, causal=w.causal)
+    out_o, lse_o = oracle.fwd(q, k, v, w.patterns, causal=w.causal)
     dt = time.perf_counter() - t0
     full = dt * w.H / heads
+    parity = None
+    if out_gpu is not None:
+        og = out_gpu.float().cpu().numpy().astype(np.float64)[:, :, :heads]
+        lg = lse_gpu.cpu().numpy().astype(np.float64)[:, :heads]
+        parity = parity_figures(og, lg, out_o, lse_o)
     return {
         "value": w.tokens / full,
         "unit": "tokens/s",
@@ -99,6 +129,8 @@ def cpu_baseline(w, heads):
         "kind": "oracle",
         "sample": f"heads 0-{heads - 1} of {w.H} of the same workload (all {w.B * w.N} tokens, "
                   f"all patterns), fp64 C oracle, {dt:.2f} s measured, scaled by {w.H}/{heads}",
+        "oracle_seconds": round(dt, 3),
+        "parity_vs_gpu": parity,
     }
 
 
@@ -129,18 +161,29 @@ def oracle_row_sample(w, per_head):
     return np.array(rows, dtype=np.int64)
 
 
-def cpu_baseline_sampled(w, q, k, v, per_head):
+def cpu_baseline_sampled(w, q, k, v, per_head, out_gpu=None, lse_gpu=None):
     """The row-wise oracle (as it stands) on a deterministic row sample of a
     device-generated workload, with the time extrapolated linearly to all
-    B * N * H rows."""
+    B * N * H rows. With the GPU's out and lse its rows are compared with
+    the oracle's at the sampled rows."""
+    import numpy as np
+
     import oracle
     from sparse_long_sequence_attn_amd.workloads import from_torch_bits
 
     qh, kh, vh = (from_torch_bits(x) for x in (q, k, v))
     rows = oracle_row_sample(w, per_head)
     t0 = time.perf_counter()
-    oracle.rows(qh, kh, vh, w.patterns, rows, causal=w.causal)
+    out_o, lse_o = oracle.rows(qh, kh, vh, w.patterns, rows, causal=w.causal)
     dt = time.perf_counter() - t0
+    parity = None
+    if out_gpu is not None:
+        import torch
+
+        idx = torch.as_tensor(rows, device=out_gpu.device)
+        og = out_gpu[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+        lg = lse_gpu[idx[:, 0], idx[:, 2], idx[:, 1]].cpu().numpy().astype(np.float64)
+        parity = parity_figures(og, lg, out_o, lse_o)
     total = w.B * w.N * w.H
     full = dt * total / len(rows)
     return {
@@ -154,6 +197,8 @@ def cpu_baseline_sampled(w, q, k, v, per_head):
                   f"of the same workload, fp64 C row-wise oracle, {dt:.2f} s measured; value is "
                   f"a LINEAR EXTRAPOLATION by row count to all {total} rows "
                   f"({full:.0f} s estimated)",
+        "oracle_seconds": round(dt, 3),
+        "parity_vs_gpu": parity,
     }
 
 
@@ -453,7 +498,7 @@ def main():
     ap.add_argument("--workload", default="paper_mixture_n32768_h16_bf16")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the workload the CPU oracle is timed on")
-    ap.add_argument("--cpu-rows-per-head", type=int, default=8192,
+    ap.add_argument("--cpu-rows-per-head", type=int, default=32768,
                     help="rows per head of the CPU oracle's sample on device-generated "
                          "workloads (the million-token one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -640,10 +685,12 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
+        # the last timed forward's out and lse are compared with the oracle's
         if w.device_generated:
-            result["cpu_baseline"] = cpu_baseline_sampled(w, q, k, v, args.cpu_rows_per_head)
+            result["cpu_baseline"] = cpu_baseline_sampled(w, q, k, v, args.cpu_rows_per_head,
+                                                          prob.out, prob.lse)
         else:
-            result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H))
+            result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_heads, w.H), prob.out, prob.lse)
     print(json.dumps(result), flush=True)
 
 

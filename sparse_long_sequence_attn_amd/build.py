@@ -35,9 +35,11 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags. The attention kernel never produces NaN (masked
-# scores are -inf and every processed row has a finite maximum), so max
-# operations need no NaN canonicalisation.
+# Per-source extra flags. The attention kernel's scores and maxima are never
+# NaN (masked scores are -inf and every processed row has a finite maximum),
+# so max operations need no NaN canonicalisation. (The bf16 row-sum MFMA can
+# see 0 * inf on a tile whose probabilities overflow; that tile's overflow
+# test compares bit patterns, which this flag cannot fold away.)
 EXTRA = {"attn_kernel.hip": ["-fno-honor-nans"]}
 
 

@@ -17,11 +17,13 @@
 //     row-major with padded rows, and the PV operand (4 keys of one head
 //     dimension per lane) is fetched with the LDS transpose read;
 //   * S^T = K Q^T and O^T += V^T P^T run on MFMA 32x32 blocks. With S^T, a
-//     lane holds one query and 16 keys of a block, so row max and row sum
-//     are in-lane except for one exchange with the lane 32 apart.
-// bf16 inputs use v_mfma_f32_32x32x16_bf16 (P rounded to bf16 for PV, the
-// row sum taken over the same rounded values); fp32 inputs use
-// v_mfma_f32_32x32x2_f32 with P kept in fp32.
+//     lane holds one query and 16 keys of a block, so the row max is in-lane
+//     except for one exchange with the lane 32 apart.
+// bf16 inputs use v_mfma_f32_32x32x16_bf16 (P rounded to bf16 for PV) and
+// take the row sums over the same rounded values on the matrix cores too
+// (v_mfma_f32_16x16x32_bf16 against a 0/1 selector): on the vector ALU the
+// sums cost more issue slots than the exponentials' overlap with the MFMAs
+// leaves. fp32 inputs use v_mfma_f32_32x32x2_f32 with P kept in fp32.
 #include <type_traits>
 
 #include "da_common.hpp"
@@ -430,7 +432,26 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
   }
   const float sl2 = a.sl2;
   const int m16 = lane & 15, g16 = lane >> 4;
-  bool started = false;  // a tile has set the running max (wave-uniform)
+  bool started = false;
+  // bf16 row sums run on the matrix cores: a 16x16x32 MFMA with this 0/1
+  // A operand (lane l holds A[l % 16][8 (l / 16) ..]) and a P fragment as B
+  // puts in lane l the row sum of query l % 16 (lanes 0-15), l - 16
+  // (16-47) or l - 32 (48-63): rows 0-7 of A take the key groups of the
+  // lanes that hold queries 0-15, rows 8-15 those of queries 16-31. The
+  // running sum stays in that lane order; sum_lane moves a per-query value
+  // (lane n and n + 32 hold query n) into it, own_lane moves the sum back.
+  const bf16x8 ksel = ((lane & 15) < 8) == ((g16 & 1) == 0)
+                          ? bf16x8{(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f,
+                                   (__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f}
+                          : bf16x8{};
+  auto sum_lane = [&](float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return g16 == 1 ? __uint_as_float(r[0]) : g16 == 2 ? __uint_as_float(r[1]) : x;
+  };
+  auto own_lane = [&](float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return g16 == 1 || g16 == 2 ? __uint_as_float(hh ? r[0] : r[1]) : x;
+  };  // a tile has set the running max (wave-uniform)
   int32_t qs_s[QB];      // first query of each of the wave's query blocks
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) qs_s[qb] = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
@@ -550,11 +571,12 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
       // The first tile of a row sets its running max m (log2 domain); later
       // tiles form p = 2^(s sl2 - m) against it without a max of their own
       // (p may exceed 1: fp32 sums and bf16 probabilities carry that
-      // exactly as well). Only when a tile's sum over one lane's keys
-      // reaches 2^32 (or overflows) is the tile redone against
-      // max(m, its max), with O and l rescaled first; O then stays below
-      // 2^53 times the largest |v|. P is rounded to bf16 once: the same
-      // packed registers feed the PV MFMA and the row sum.
+      // exactly as well). Only when some row's sum over the tile reaches
+      // 2^32 (or overflows) is the tile redone against max(m, its max), with
+      // O and l rescaled first; O then stays far inside the fp32 range (each
+      // tile adds less than 2^32 times the largest |v|, a row sees fewer
+      // than 2^26 tiles). P is rounded to bf16 once: the same packed
+      // registers feed the PV MFMA and the row-sum MFMA.
       if (!started) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) m_run[qb] = tile_max(qb);
@@ -565,7 +587,6 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
       auto form_p = [&]() {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          float ls[2] = {0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
@@ -576,24 +597,32 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
               pr[0] = (__bf16)p0;
               pr[1] = (__bf16)p1;
               pw[qb][c][e >> 1] = __builtin_bit_cast(uint32_t, pr);
-              const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-              ls[c & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, ls[c & 1], false);
             }
           }
-          lsum[qb] = ls[0] + ls[1];
+          f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 2 * KB; ++c)
+            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ksel, __builtin_bit_cast(bf16x8, pw[qb][c]), t,
+                                                        0, 0, 0);
+          lsum[qb] = t[0];
         }
       };
       form_p();
+      // A p that overflowed to inf turns the row-sum MFMA's zero-weighted
+      // terms into NaN. The test is on the bit pattern (sums are >= 0, and
+      // NaN and inf order above 2^32 as integers) because this file is
+      // compiled assuming no NaN, which would let a float comparison miss it.
       bool over = false;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) over = over || !(lsum[qb] < 4294967296.f);
+      for (int qb = 0; qb < QB; ++qb)
+        over = over || __float_as_uint(lsum[qb]) >= __float_as_uint(4294967296.f);
       if (__ballot(over) != 0) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const float m_new = fmaxf(m_run[qb], tile_max(qb));
           const float alpha = exp2_fast(m_run[qb] - m_new);
           m_run[qb] = m_new;
-          l_run[qb] *= alpha;
+          l_run[qb] *= sum_lane(alpha);
 #pragma unroll
           for (int db = 0; db < 2; ++db) O[db][qb] *= alpha;
         }
@@ -744,7 +773,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
   // ---- epilogue: normalise every valid query row and write it
   float l_tot[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l_tot[qb] = pair_sum(l_run[qb]);
+  for (int qb = 0; qb < QB; ++qb) l_tot[qb] = BF ? own_lane(l_run[qb]) : pair_sum(l_run[qb]);
   T* const orow = reinterpret_cast<T*>(a.out) + headbase;
   float* const lse_row = a.lse + ((int64_t)tl.b * a.H + tl.h) * a.N;
   const int64_t seg_end = seg0 + wp;
