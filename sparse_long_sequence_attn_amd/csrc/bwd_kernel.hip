@@ -385,7 +385,7 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
     if (tid < BQ) {
       float* ls = reinterpret_cast<float*>(base + 2 * kTileBytes);
       ls[tid] = lreg * kLog2e;
-      ls[BQ + tid] = dreg;
+      ls[BQ + tid] = -dreg;  // -D: the dP products accumulate onto it
     }
   };
 
@@ -401,16 +401,25 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
     const T* Qs = reinterpret_cast<const T*>(base);
     const T* Ds = reinterpret_cast<const T*>(base + kTileBytes);
     const float* ls = reinterpret_cast<const float*>(base + 2 * kTileBytes);
-    const float* dd = ls + BQ;
+    const float* ndd = ls + BQ;  // -D per query row
 #pragma unroll
     for (int qb = 0; qb < QBT; ++qb) {
       const int32_t qs = qstart + t * BQ + 32 * qb;  // first query of the block
       if (qs >= g.L) break;
       if (CAUSAL && qs < kw0) continue;  // 32-aligned: every query precedes every key
       const int row = qb * 32 + n;
+      // dP starts at -D of its query (register v: query qb*32 + 8(v/4) +
+      // 4hh + v%4), so the products leave dP - D for dS = P (dP - D)
       f32x16 S, dP;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) S[v] = dP[v] = 0.f;
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x4 nd4 = *reinterpret_cast<const f32x4*>(ndd + qb * 32 + 8 * gq + 4 * hh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          S[4 * gq + j] = 0.f;
+          dP[4 * gq + j] = nd4[j];
+        }
+      }
       if constexpr (BF) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -440,14 +449,13 @@ __global__ __launch_bounds__(NW * 64, BF ? 3 : 1) void bwd_kv_kernel(const BwdAr
         for (int gq = 0; gq < 4; ++gq) {
           const int qi = qb * 32 + 8 * gq + 4 * hh;
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qi);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dd + qi);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int v = 4 * gq + j;
             float p = __builtin_amdgcn_exp2f(fmaf(S[v], sl2, -l4[j]));
             if (diag && 8 * gq + 4 * hh + j < n) p = 0.f;
             pv[v] = p;
-            sv[v] = p * (dP[v] - d4[j]);
+            sv[v] = p * dP[v];
           }
           if constexpr (BF) {
 #pragma unroll
