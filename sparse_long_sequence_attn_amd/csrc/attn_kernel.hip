@@ -432,7 +432,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
   }
   const float sl2 = a.sl2;
   const int m16 = lane & 15, g16 = lane >> 4;
-  bool started = false;
+  bool started = false;  // a tile has set the running max (wave-uniform)
   // bf16 row sums run on the matrix cores: a 16x16x32 MFMA with this 0/1
   // A operand (lane l holds A[l % 16][8 (l / 16) ..]) and a P fragment as B
   // puts in lane l the row sum of query l % 16 (lanes 0-15), l - 16
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(NW * 64, QKN ? (BF ? 3 : 2) : 4) void attn_fwd_kern
   auto own_lane = [&](float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return g16 == 1 || g16 == 2 ? __uint_as_float(hh ? r[0] : r[1]) : x;
-  };  // a tile has set the running max (wave-uniform)
+  };
   int32_t qs_s[QB];      // first query of each of the wave's query blocks
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) qs_s[qb] = __builtin_amdgcn_readfirstlane(qw0 + 32 * qb);
