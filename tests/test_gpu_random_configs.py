@@ -10,6 +10,8 @@ lse 1e-4 / 4e-3 (test_gpu_parity.py derives them), gradients the same bar
 relative to each tensor's scale (test_gpu_bwd.py). Outputs are pre-filled
 with NaN; rows no pattern gathers must be exactly 0 / -inf / 0.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -22,7 +24,8 @@ pytestmark = pytest.mark.gpu
 
 TOL_OUT = {"f32": 1e-4, "bf16": 2e-2}
 TOL_LSE = {"f32": 1e-4, "bf16": 4e-3}
-N_CASES = 24
+# more cases for a longer sweep: DA_RANDOM_CASES=324 python -m pytest tests/test_gpu_random_configs.py
+N_CASES = int(os.environ.get("DA_RANDOM_CASES", "24"))
 
 
 def draw_case(i):
