@@ -77,6 +77,28 @@ def cpu_model():
     return None
 
 
+def gpu_max_sclk_mhz():
+    """The gfx950 agent's maximum engine clock as rocminfo reports it (MHz),
+    or None. The published bf16 peak assumes 2400 MHz."""
+    import subprocess
+
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    seen_gpu = False  # the agent's own attributes follow its Name line
+    for line in txt.splitlines():
+        key, _, val = line.partition(":")
+        if key.strip() == "Name" and val.strip() == "gfx950":
+            seen_gpu = True
+        elif seen_gpu and key.strip() == "Max Clock Freq. (MHz)":
+            try:
+                return int(val.split()[0])
+            except (IndexError, ValueError):
+                return None
+    return None
+
+
 def parity_figures(out_gpu, lse_gpu, out_o, lse_o):
     """Max-abs errors of the GPU result against the oracle's on the same
     elements, the output error in units of the bf16 spacing at the oracle's
@@ -639,6 +661,9 @@ def main():
     roof["traffic"] = measured_traffic("fwd", w.name)
     roof["kernel"] = "attn_fwd_kernel"
     roof["kernel_ms"] = round(attn_ms, 4)
+    # the published peak's clock, checked against the agent's own figure
+    sclk = gpu_max_sclk_mhz()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
     result = {
         "metric": METRIC,
@@ -682,6 +707,9 @@ def main():
             "onepass_tflops_algorithmic": round(c.flops_alg / (onepass_ms / 1e3) / 1e12, 2)
             if onepass_ms else None,
             "device": torch.cuda.get_device_name(dev),
+            "max_sclk_mhz": sclk,
+            "bf16_peak_at_max_sclk_tflops": round(cus * 4096 * sclk * 1e6 / 1e12, 1)
+            if sclk else None,
         },
     }
     if not args.no_cpu_baseline:
