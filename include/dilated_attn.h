@@ -28,9 +28,10 @@
  *
  * Memory and ownership: every pointer except `patterns` (host) and the
  * stream handle is DEVICE memory owned by the caller. The library allocates
- * nothing, keeps no pointer after a call returns and has no mutable global
- * state, so calls on different streams may run concurrently as long as they
- * do not share output or workspace buffers.
+ * nothing and keeps no pointer after a call returns. Its only mutable global
+ * state is the per-GPU device array behind dilated_attn_fwd_noalloc (see
+ * there); every other call may run concurrently with others on different
+ * streams as long as they do not share output or workspace buffers.
  *
  * Asynchrony: compute calls enqueue kernels on `stream` (a hipStream_t; NULL
  * is the default stream) and return without synchronising. Faults during
