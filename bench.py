@@ -77,26 +77,21 @@ def cpu_model():
     return None
 
 
-def gpu_max_sclk_mhz():
-    """The gfx950 agent's maximum engine clock as rocminfo reports it (MHz),
-    or None. The published bf16 peak assumes 2400 MHz."""
-    import subprocess
+def gpu_max_sclk_mhz(device=0):
+    """The device's peak engine clock as the HIP runtime reports it (MHz),
+    or None. The published bf16 peak assumes 2400 MHz. Asked in-process (no
+    child process, which a profiler would follow)."""
+    import ctypes
 
     try:
-        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=30).stdout
-    except (OSError, subprocess.SubprocessError):
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
         return None
-    seen_gpu = False  # the agent's own attributes follow its Name line
-    for line in txt.splitlines():
-        key, _, val = line.partition(":")
-        if key.strip() == "Name" and val.strip() == "gfx950":
-            seen_gpu = True
-        elif seen_gpu and key.strip() == "Max Clock Freq. (MHz)":
-            try:
-                return int(val.split()[0])
-            except (IndexError, ValueError):
-                return None
-    return None
+    khz = ctypes.c_int(0)
+    # hipDeviceGetAttribute(&value, hipDeviceAttributeClockRate (= 5, kHz), device)
+    if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, int(device)) != 0 or khz.value <= 0:
+        return None
+    return khz.value // 1000
 
 
 def parity_figures(out_gpu, lse_gpu, out_o, lse_o):
@@ -662,7 +657,7 @@ def main():
     roof["kernel"] = "attn_fwd_kernel"
     roof["kernel_ms"] = round(attn_ms, 4)
     # the published peak's clock, checked against the agent's own figure
-    sclk = gpu_max_sclk_mhz()
+    sclk = gpu_max_sclk_mhz(dev.index or 0)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
     result = {

@@ -1,7 +1,7 @@
 """Host-side helpers of bench.py (no GPU): the GPU clock parser and the
 parity summary it prints next to the CPU baseline."""
+import ctypes
 import os
-import subprocess
 import sys
 
 import numpy as np
@@ -9,44 +9,37 @@ import numpy as np
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import bench  # noqa: E402
 
-ROCMINFO = """*******
-Agent 1
-*******
-  Name:                    AMD EPYC 9575F 64-Core Processor
-  Max Clock Freq. (MHz):   3300
-*******
-Agent 2
-*******
-  Name:                    gfx950
-  Marketing Name:          AMD Instinct MI355X
-  Max Clock Freq. (MHz):   2400
-  ISA Info:
-    ISA 1
-      Name:                    amdgcn-amd-amdhsa--gfx950:sramecc+:xnack-
-"""
+class _FakeHip:
+    """Stands in for the HIP runtime: hipDeviceGetAttribute writes `khz`."""
+
+    def __init__(self, khz, rc=0):
+        self.khz, self.rc, self.calls = khz, rc, []
+
+    def hipDeviceGetAttribute(self, ptr, attr, dev):
+        self.calls.append((attr, dev))
+        ptr._obj.value = self.khz
+        return self.rc
 
 
-class _Done:
-    def __init__(self, stdout):
-        self.stdout = stdout
+def test_max_sclk_from_the_runtime_clock_rate(monkeypatch):
+    fake = _FakeHip(2400000)
+    monkeypatch.setattr(ctypes, "CDLL", lambda name: fake)
+    assert bench.gpu_max_sclk_mhz(0) == 2400
+    assert fake.calls == [(5, 0)]  # hipDeviceAttributeClockRate
 
 
-def test_max_sclk_is_the_gpu_agents(monkeypatch):
-    monkeypatch.setattr(subprocess, "run", lambda *a, **k: _Done(ROCMINFO))
-    assert bench.gpu_max_sclk_mhz() == 2400
+def test_max_sclk_none_on_a_failed_query(monkeypatch):
+    monkeypatch.setattr(ctypes, "CDLL", lambda name: _FakeHip(2400000, rc=1))
+    assert bench.gpu_max_sclk_mhz(0) is None
+    monkeypatch.setattr(ctypes, "CDLL", lambda name: _FakeHip(0))
+    assert bench.gpu_max_sclk_mhz(0) is None
 
 
-def test_max_sclk_absent_without_a_gfx950_agent(monkeypatch):
-    cpu_only = ROCMINFO.split("*******\nAgent 2")[0]
-    monkeypatch.setattr(subprocess, "run", lambda *a, **k: _Done(cpu_only))
-    assert bench.gpu_max_sclk_mhz() is None
-
-
-def test_max_sclk_when_rocminfo_is_missing(monkeypatch):
-    def missing(*a, **k):
-        raise FileNotFoundError("rocminfo")
-    monkeypatch.setattr(subprocess, "run", missing)
-    assert bench.gpu_max_sclk_mhz() is None
+def test_max_sclk_none_without_the_runtime(monkeypatch):
+    def missing(name):
+        raise OSError(name)
+    monkeypatch.setattr(ctypes, "CDLL", missing)
+    assert bench.gpu_max_sclk_mhz(0) is None
 
 
 def test_parity_figures_counts_bf16_spacings():
