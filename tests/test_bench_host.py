@@ -1,5 +1,6 @@
-"""Host-side helpers of bench.py (no GPU): the GPU clock parser and the
-parity summary it prints next to the CPU baseline."""
+"""Host-side helpers of bench.py (no GPU): the peak-clock query (against a
+stand-in for the HIP runtime) and the parity summary it prints next to the
+CPU baseline."""
 import ctypes
 import os
 import sys
