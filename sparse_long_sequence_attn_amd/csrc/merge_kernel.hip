@@ -36,8 +36,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kLanesPerRow = 4;
 constexpr int kDimsPerLane = kDh / kLanesPerRow;  // 16
 constexpr int kVecPerLane = kDimsPerLane / 4;      // float4 loads per partial row
-constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / kLanesPerRow;  // 64
+constexpr int kThreads = 128;
+constexpr int kRowsPerBlock = kThreads / kLanesPerRow;  // 32
 
 __device__ inline uint32_t pack_bf16(float x, float y) {
   bf16x2 p;
